@@ -1,0 +1,225 @@
+"""CPU oracle for the structured-grid stencil sweeps -- TEST INFRASTRUCTURE.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its Python binding) never imports it and never falls back to it.
+
+The arithmetic lives in ``oracle.c`` (plain single-threaded C built with
+``-O2 -ffp-contract=off``); this module only builds it with gcc and marshals
+numpy arrays.  It shares no code with the HIP library.
+
+Array conventions (all numpy, C-contiguous):
+
+* 2D grid ``u(nx, ny)`` column-major with leading dimension ``ld``: a numpy
+  array of shape ``(ny, ld)``; logical columns are ``[:, :nx]``.
+* field ``f_var(j, k, l)``: numpy shape ``(nz, ny, nx)``; nvar fields stacked
+  as ``(nvar, nz, ny, nx)``.
+* packed output: x -> ``(nvar, nz, ny, nx)``, y -> ``(nvar, nz, nx, ny)``,
+  z -> ``(nvar, nx, ny, nz)`` (first Fortran index last in numpy).
+* faces per variable: Fx ``(nz, ny, nx+1)``, Fy ``(nz, ny+1, nx)``,
+  Fz ``(nz+1, ny, nx)``; rhs ``(nvar, nz, ny, nx)``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import time
+from pathlib import Path
+
+import numpy as np
+
+_HERE = Path(__file__).resolve().parent
+_SRC = _HERE / "oracle.c"
+_LIB = _HERE / "liboracle.so"
+
+GCC_FLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c99",
+             "-Wall", "-Wextra", "-shared", "-fPIC"]
+
+
+def build(force: bool = False) -> Path:
+    """Compile oracle.c into liboracle.so with gcc (contraction off)."""
+    if force or not _LIB.exists() or _LIB.stat().st_mtime < _SRC.stat().st_mtime:
+        tmp = _LIB.with_suffix(".so.tmp%d" % os.getpid())
+        subprocess.run(["gcc", *GCC_FLAGS, str(_SRC), "-o", str(tmp)], check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        lib = ctypes.CDLL(str(build()))
+        i64, i32, vp, dbl = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_double
+        for name in ("oracle_diffuse2d_f64", "oracle_diffuse2d_f32"):
+            fn = getattr(lib, name)
+            fn.argtypes = [vp, vp, i64, i64, i64, dbl, i64]
+            fn.restype = ctypes.c_int
+        lib.oracle_field_pack.argtypes = [vp, i32, i64, i64, i64, i32, vp]
+        lib.oracle_field_pack.restype = ctypes.c_int
+        lib.oracle_field_unpack.argtypes = [vp, i32, i64, i64, i64, i32, vp]
+        lib.oracle_field_unpack.restype = ctypes.c_int
+        lib.oracle_flux_diff.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i64, i64, vp]
+        lib.oracle_flux_diff.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray) -> int:
+    assert a.flags.c_contiguous
+    return a.ctypes.data
+
+
+def _ptr_table(arrs) -> ctypes.Array:
+    tab = (ctypes.c_void_p * len(arrs))()
+    for n, a in enumerate(arrs):
+        tab[n] = _ptr(a)
+    return tab
+
+
+# ---------------------------------------------------------------------------
+# 2D five-point diffusion
+# ---------------------------------------------------------------------------
+
+def diffuse2d(u: np.ndarray, v: np.ndarray, nx: int, alpha: float, steps: int) -> bool:
+    """Advance ``steps`` five-point sweeps in place on the ping-pong pair.
+
+    ``u`` and ``v`` are ``(ny, ld)`` float32 or float64 arrays.  Both edge
+    rings are zeroed first.  Returns True if the result is in ``v`` (odd step
+    count), False if it is in ``u``.
+    """
+    assert u.shape == v.shape and u.dtype == v.dtype and u.ndim == 2
+    ny, ld = u.shape
+    assert 3 <= nx <= ld and ny >= 3 and steps >= 0
+    lib = _load()
+    fn = lib.oracle_diffuse2d_f64 if u.dtype == np.float64 else lib.oracle_diffuse2d_f32
+    assert u.dtype in (np.float64, np.float32)
+    return bool(fn(_ptr(u), _ptr(v), nx, ny, ld, float(alpha), int(steps)))
+
+
+def diffuse2d_result(u0: np.ndarray, nx: int, alpha: float, steps: int) -> np.ndarray:
+    """Copying convenience: run from ``u0`` with ``v`` = 0, return the result grid."""
+    u = np.array(u0, copy=True, order="C")
+    v = np.zeros_like(u)
+    return v if diffuse2d(u, v, nx, alpha, steps) else u
+
+
+def diffuse2d_window(u0: np.ndarray, nx: int, alpha: float, steps: int,
+                     i: int, j: int) -> float:
+    """Value of cell (i, j) of the full-grid result, computed on a sub-grid.
+
+    After ``steps`` sweeps a cell depends only on cells within Manhattan
+    distance ``steps``.  The sub-grid keeps every such cell; where it is cut
+    inside the grid the cut ring lies more than ``steps`` away from (i, j), so
+    the artificial zero edge the oracle puts there cannot reach it.
+    """
+    ny = u0.shape[0]
+    r = steps + 1
+    i0, i1 = max(0, i - r), min(nx, i + r + 1)
+    j0, j1 = max(0, j - r), min(ny, j + r + 1)
+    sub = np.ascontiguousarray(u0[j0:j1, i0:i1])
+    # Grid edges that survive in the window are real edges; cut sides become
+    # window edges that the oracle zeroes, which is harmless (see above).
+    res = diffuse2d_result(sub, i1 - i0, alpha, steps)
+    return res[j - j0, i - i0]
+
+
+# ---------------------------------------------------------------------------
+# Directional pack / unpack
+# ---------------------------------------------------------------------------
+
+PACK_SHAPE = {0: lambda nx, ny, nz: (nz, ny, nx),
+              1: lambda nx, ny, nz: (nz, nx, ny),
+              2: lambda nx, ny, nz: (nx, ny, nz)}
+
+
+def field_pack(fields: np.ndarray, direction: int) -> np.ndarray:
+    """Pack ``fields`` of shape (nvar, nz, ny, nx) along x (0), y (1) or z (2)."""
+    assert fields.dtype == np.float64 and fields.ndim == 4
+    nvar, nz, ny, nx = fields.shape
+    fl = [np.ascontiguousarray(fields[v]) for v in range(nvar)]
+    out = np.empty((nvar,) + PACK_SHAPE[direction](nx, ny, nz), dtype=np.float64)
+    rc = _load().oracle_field_pack(_ptr_table(fl), nvar, nx, ny, nz, direction, _ptr(out))
+    assert rc == 0
+    return out
+
+
+def field_unpack(packed: np.ndarray, nx: int, ny: int, nz: int, direction: int) -> np.ndarray:
+    """Inverse of :func:`field_pack`; returns (nvar, nz, ny, nx)."""
+    nvar = packed.shape[0]
+    out = np.empty((nvar, nz, ny, nx), dtype=np.float64)
+    fl = [out[v] for v in range(nvar)]
+    rc = _load().oracle_field_unpack(_ptr(np.ascontiguousarray(packed)), nvar, nx, ny, nz,
+                                     direction, _ptr_table(fl))
+    assert rc == 0
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Conservative flux difference
+# ---------------------------------------------------------------------------
+
+def flux_diff(fx, fy, fz, dx, dy, dz) -> np.ndarray:
+    """rhs (nvar, nz, ny, nx) from per-variable face arrays.
+
+    ``fx`` (nvar, nz, ny, nx+1), ``fy`` (nvar, nz, ny+1, nx), ``fz``
+    (nvar, nz+1, ny, nx) or None for the 2D form (then nz must be 1).
+    """
+    nvar, nz, ny, nxp1 = fx.shape
+    nx = nxp1 - 1
+    assert fy.shape == (nvar, nz, ny + 1, nx)
+    if fz is not None:
+        assert fz.shape == (nvar, nz + 1, ny, nx)
+    else:
+        assert nz == 1
+    fxl = [np.ascontiguousarray(fx[v]) for v in range(nvar)]
+    fyl = [np.ascontiguousarray(fy[v]) for v in range(nvar)]
+    fzl = [np.ascontiguousarray(fz[v]) for v in range(nvar)] if fz is not None else None
+    dx = np.ascontiguousarray(dx, dtype=np.float64)
+    dy = np.ascontiguousarray(dy, dtype=np.float64)
+    rhs = np.empty((nvar, nz, ny, nx), dtype=np.float64)
+    if fz is not None:
+        dz = np.ascontiguousarray(dz, dtype=np.float64)
+        fz_tab, dz_p = _ptr_table(fzl), _ptr(dz)
+    else:
+        fz_tab, dz_p = None, None
+    rc = _load().oracle_flux_diff(_ptr_table(fxl), _ptr_table(fyl), fz_tab,
+                                  _ptr(dx), _ptr(dy), dz_p, nvar, nx, ny, nz, _ptr(rhs))
+    assert rc == 0
+    return rhs
+
+
+# ---------------------------------------------------------------------------
+# Comparison metrics (Qiita Part 3, section 8 and 8.1: max abs, RMSE,
+# relative L2, mass difference, worst index, failures under
+# |ref - test| <= atol + rtol*|ref|).
+# ---------------------------------------------------------------------------
+
+def compare(ref: np.ndarray, cand: np.ndarray, atol: float, rtol: float) -> dict:
+    """Error metrics of ``cand`` against ``ref`` over all cells, in float64."""
+    import math
+    r = np.asarray(ref, dtype=np.float64).ravel()
+    c = np.asarray(cand, dtype=np.float64).ravel()
+    assert r.shape == c.shape
+    d = np.abs(r - c)
+    sq_err = math.fsum((d * d).tolist())
+    sq_ref = math.fsum((r * r).tolist())
+    return {
+        "max_abs": float(d.max()),
+        "rmse": math.sqrt(sq_err / r.size),
+        "relative_l2": math.sqrt(sq_err / sq_ref) if sq_ref else math.sqrt(sq_err),
+        "mass_difference": math.fsum(c.tolist()) - math.fsum(r.tolist()),
+        "worst_index_0based": int(np.argmax(d)),
+        "failures": int(np.count_nonzero(d > atol + rtol * np.abs(r))),
+        "cells": int(r.size),
+    }
+
+
+def timed(fn, *args, **kw):
+    """(result, seconds) of one call, wall clock around the compute only."""
+    t0 = time.perf_counter()
+    out = fn(*args, **kw)
+    return out, time.perf_counter() - t0

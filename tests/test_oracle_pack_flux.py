@@ -1,0 +1,186 @@
+"""Pins of the CPU oracle's directional pack and conservative flux difference
+(no GPU needed).
+
+Sources: MFC pull request 2087, "SCC26: Collapse only spatial loops in
+per-variable GPU kernels", Changes (the WENO input pack
+v_rs_weno(j,k,l,i) = v_vf(i)%sf(j,k,l); x/y/z flux differences with the
+inverse spacing formed once per cell).  The y/z pack index orders
+out(k,j,l,var) / out(l,k,j,var) and the (F_lo - F_hi)*inv_d form are the
+workload definitions' readings.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from structured_grid_cfd_amd import inputs
+
+SHAPES = [(5, 4, 3), (7, 1, 6), (1, 6, 5), (9, 8, 1), (3, 3, 3)]
+
+
+# ---------------------------------------------------------------------------
+# pack
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("nx,ny,nz", SHAPES)
+@pytest.mark.parametrize("direction", [0, 1, 2])
+def test_pack_matches_axis_permutation(nx, ny, nz, direction):
+    """The pack reduces to numpy's axis permutation of the (nvar, l, k, j)
+    array: x keeps (var, l, k, j); y gives (var, l, j, k); z gives
+    (var, j, k, l)."""
+    f = inputs.normal_fields(3, nx, ny, nz, seed=nx + 10 * ny + 100 * nz)
+    out = oracle.field_pack(f, direction)
+    axes = {0: (0, 1, 2, 3), 1: (0, 1, 3, 2), 2: (0, 3, 2, 1)}[direction]
+    assert np.array_equal(out, np.transpose(f, axes))
+
+
+def test_x_pack_is_concatenation():
+    """Along x the packed array is the variables' arrays one after another."""
+    f = inputs.normal_fields(4, 6, 5, 4, seed=2)
+    out = oracle.field_pack(f, 0)
+    assert np.array_equal(out.ravel(), np.concatenate([f[v].ravel() for v in range(4)]))
+
+
+@pytest.mark.parametrize("direction", [0, 1, 2])
+def test_pack_is_a_permutation(direction):
+    """Distinct inputs: the multiset of values is preserved, every output
+    slot is written exactly once, and each value sits where its index says."""
+    nvar, nx, ny, nz = 3, 5, 4, 6
+    f = inputs.distinct_fields(nvar, nx, ny, nz)
+    out = oracle.field_pack(f, direction)
+    assert np.array_equal(np.sort(out.ravel()), np.sort(f.ravel()))
+    n = nx * ny * nz
+    # the value encodes (var, j, k, l); check the position in Fortran terms
+    for var in range(nvar):
+        for l in range(nz):
+            for k in range(ny):
+                for j in range(nx):
+                    val = j + nx * (k + ny * l) + n * var
+                    if direction == 0:
+                        got = out[var, l, k, j]
+                    elif direction == 1:
+                        got = out[var, l, j, k]
+                    else:
+                        got = out[var, j, k, l]
+                    assert got == val
+
+
+@pytest.mark.parametrize("direction", [0, 1, 2])
+def test_unpack_inverts_pack(direction):
+    f = inputs.normal_fields(5, 7, 3, 4, seed=9)
+    out = oracle.field_pack(f, direction)
+    back = oracle.field_unpack(out, 7, 3, 4, direction)
+    assert np.array_equal(back, f)
+
+
+# ---------------------------------------------------------------------------
+# flux difference
+# ---------------------------------------------------------------------------
+
+def _faces(nvar, nx, ny, nz, seed, two_d=False):
+    return inputs.normal_faces(nvar, nx, ny, nz, seed, two_d)
+
+
+@pytest.mark.parametrize("two_d", [False, True])
+def test_constant_fluxes_give_zero(two_d):
+    """Equal fluxes on both faces of every cell: rhs is +0.0 bitwise."""
+    nvar, nx, ny, nz = 3, 6, 5, (1 if two_d else 4)
+    fi = _faces(nvar, nx, ny, nz, 1, two_d)
+    fi.fx[:] = 2.5
+    fi.fy[:] = -1.25
+    if not two_d:
+        fi.fz[:] = 3.0
+    rhs = oracle.flux_diff(fi.fx, fi.fy, fi.fz, fi.dx, fi.dy, fi.dz)
+    assert np.all(rhs == 0) and not np.any(np.signbit(rhs))
+
+
+def test_linear_fluxes_dyadic_spacing_exact():
+    """F(face index) = c*index with d = 2^-m: each term is (F_lo - F_hi)/d =
+    -c*2^m exactly, so rhs = -(cx*2^mx + cy*2^my + cz*2^mz) for every cell.
+    Pins the sign (low face minus high face) and the face index (j, j+1)."""
+    nvar, nx, ny, nz = 2, 5, 4, 3
+    fi = _faces(nvar, nx, ny, nz, 2)
+    cx, cy, cz = 3.0, -5.0, 7.0
+    fi.fx[:] = cx * np.arange(nx + 1)[None, None, None, :]
+    fi.fy[:] = cy * np.arange(ny + 1)[None, None, :, None]
+    fi.fz[:] = cz * np.arange(nz + 1)[None, :, None, None]
+    fi.dx[:], fi.dy[:], fi.dz[:] = 2.0 ** -3, 2.0 ** -1, 2.0 ** -4
+    rhs = oracle.flux_diff(fi.fx, fi.fy, fi.fz, fi.dx, fi.dy, fi.dz)
+    assert np.all(rhs == -(cx * 8 + cy * 2 + cz * 16))
+
+
+def test_telescoping_sum_dyadic():
+    """sum_j rhs_x(j,k,l) * dx[j] = Fx(0,k,l) - Fx(nx,k,l) exactly when all
+    values are dyadic (small integers, power-of-two widths); with zero y and z
+    fluxes rhs is the x term alone.  Same along y and z."""
+    nvar, nx, ny, nz = 2, 6, 5, 4
+    g = np.random.Generator(np.random.PCG64(5))
+    fi = _faces(nvar, nx, ny, nz, 3)
+    for axis in ("x", "y", "z"):
+        fx = np.zeros_like(fi.fx)
+        fy = np.zeros_like(fi.fy)
+        fz = np.zeros_like(fi.fz)
+        d = {"x": fx, "y": fy, "z": fz}[axis]
+        d[:] = g.integers(-50, 50, d.shape).astype(np.float64)
+        dx = 2.0 ** -g.integers(0, 4, nx).astype(np.float64)
+        dy = 2.0 ** -g.integers(0, 4, ny).astype(np.float64)
+        dz = 2.0 ** -g.integers(0, 4, nz).astype(np.float64)
+        rhs = oracle.flux_diff(fx, fy, fz, dx, dy, dz)
+        if axis == "x":
+            s = (rhs * dx[None, None, None, :]).sum(axis=3)
+            assert np.array_equal(s, fx[..., 0] - fx[..., nx])
+        elif axis == "y":
+            s = (rhs * dy[None, None, :, None]).sum(axis=2)
+            assert np.array_equal(s, fy[:, :, 0, :] - fy[:, :, ny, :])
+        else:
+            s = (rhs * dz[None, :, None, None]).sum(axis=1)
+            assert np.array_equal(s, fz[:, 0] - fz[:, nz])
+
+
+def test_zero_cross_fluxes_reduce_to_x_term():
+    """Zero y and z fluxes: rhs is (Fx_lo - Fx_hi) * (1/dx) bitwise (adding
+    +0.0 twice changes nothing)."""
+    nvar, nx, ny, nz = 2, 7, 3, 4
+    fi = _faces(nvar, nx, ny, nz, 4)
+    fy = np.zeros_like(fi.fy)
+    fz = np.zeros_like(fi.fz)
+    rhs = oracle.flux_diff(fi.fx, fy, fz, fi.dx, fi.dy, fi.dz)
+    expect = (fi.fx[..., :-1] - fi.fx[..., 1:]) * (1.0 / fi.dx)[None, None, None, :]
+    assert np.array_equal(rhs, expect)
+
+
+def _exact_rhs(fi, var, j, k, l, two_d):
+    rx = (Fraction(fi.fx[var, l, k, j]) - Fraction(fi.fx[var, l, k, j + 1])) / Fraction(fi.dx[j])
+    ry = (Fraction(fi.fy[var, l, k, j]) - Fraction(fi.fy[var, l, k + 1, j])) / Fraction(fi.dy[k])
+    r = rx + ry
+    if not two_d:
+        r += (Fraction(fi.fz[var, l, k, j]) - Fraction(fi.fz[var, l + 1, k, j])) / Fraction(fi.dz[l])
+    return r, abs(rx) + abs(ry) + (0 if two_d else abs(r - rx - ry))
+
+
+@pytest.mark.parametrize("nx,ny,nz,two_d", [(6, 5, 4, False), (4, 3, 1, True), (1, 2, 3, False)])
+def test_bruteforce_exact_rational(nx, ny, nz, two_d):
+    """Tiny grids against exact rationals with non-uniform widths on every
+    axis: each rhs within a few rounding units of the exact value (an index
+    or operand mix-up would be off by O(1))."""
+    nvar = 2
+    fi = _faces(nvar, nx, ny, nz, 6, two_d)
+    rhs = oracle.flux_diff(fi.fx, fi.fy, fi.fz, fi.dx, fi.dy, fi.dz)
+    eps = np.finfo(np.float64).eps
+    for var in range(nvar):
+        for l in range(nz):
+            for k in range(ny):
+                for j in range(nx):
+                    exact, scale = _exact_rhs(fi, var, j, k, l, two_d)
+                    assert abs(rhs[var, l, k, j] - float(exact)) <= 8 * eps * float(scale) + 1e-300
+
+
+def test_two_d_form_equals_three_d_with_zero_z():
+    """The 2D form (no Fz) equals the 3D form with nz = 1 and equal z fluxes."""
+    fi = _faces(3, 8, 6, 1, 7, two_d=True)
+    fz = np.full((3, 2, 6, 8), 0.5)
+    dz = np.array([0.25])
+    a = oracle.flux_diff(fi.fx, fi.fy, None, fi.dx, fi.dy, None)
+    b = oracle.flux_diff(fi.fx, fi.fy, fz, fi.dx, fi.dy, dz)
+    assert np.array_equal(a, b)
