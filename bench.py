@@ -1,0 +1,383 @@
+#!/usr/bin/env python3
+"""Benchmark of the structured-grid stencil sweeps on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--dtype f64|f32] [--quick]
+
+One benchmark step = one full run of the 4096x4096 explicit five-point
+diffusion workload: 1000 sweeps from a seeded interior uniform [0,1) field
+with zero edges, alpha 0.1, in the production mapping (temporal blocking).
+Inputs are resident in HBM before the timed region starts.  K steps are timed
+with HIP events on the stream the kernels run on (torch's current stream) and
+with the host clock around synchronisations.
+
+Prints ONE JSON line with:
+  value       interior cell updates per second (the cell-var rate; nvar = 1),
+  roofline    the dominant kernel (the marching sweep) against MI355X peaks:
+              algorithmic bytes per launch (one read of the grid, one write of
+              its interior) over the kernel's average launch time, and its
+              arithmetic (7 operations per interior cell per fused step) over
+              the vector-ALU peak; `bound` names the tighter one;
+  cpu_baseline  the CPU oracle (single thread) on a bounded sample of the
+              same workload, timed on this host;
+  kernels     per-kernel figures for the other workloads (pack along x/y/z,
+              flux difference, the 2D workload, the page's three loop layouts,
+              FP32, a 16-byte copy for reference), each as time, cell-var
+              updates/s and GB/s of minimal traffic with the MALL flushed
+              before every single-pass repetition.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import statistics
+import sys
+import time
+from pathlib import Path
+
+import numpy as np
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+METRIC = "cell-var updates/s and achieved HBM GB/s (% of MI355X peak), 1 GPU"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+# Vector ALU peak for the stencil's plain (non-fused, non-packed) adds and
+# multiplies: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = 39.3 T operations/s in
+# FP32 or FP64 (the published 78.6 TFLOP/s FP64 counts an FMA as two).
+ALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
+FLOPS_PER_UPDATE = 7  # W+E, +S, +N, 4*C, -, alpha*t, C+
+PROFILE_COUNTERS = ROOT / "profiles" / "diffusion_march_counters.json"
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--dtype", choices=["f64", "f32"], default="f64")
+    p.add_argument("--time-block", type=int, default=None)
+    p.add_argument("--tile-rows", type=int, default=None)
+    p.add_argument("--quick", action="store_true", help="headline only: skip the per-kernel table")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--cpu-steps", type=int, default=400,
+                   help="sweeps of the CPU-baseline sample (same grid)")
+    return p.parse_args()
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def source_hash(path: Path) -> str:
+    return hashlib.sha256(path.read_bytes()).hexdigest()[:16]
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU: the sweeps have no "
+                          "multi-GPU path", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+
+    from structured_grid_cfd_amd import binding, inputs, launch_config
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    torch.cuda.set_device(0)
+    binding.load()
+    dtype = np.float64 if args.dtype == "f64" else np.float32
+    es = 8 if args.dtype == "f64" else 4
+    cfg = launch_config.diffusion(args.dtype)
+    if args.time_block is not None:
+        cfg["time_block"] = args.time_block
+        cfg["map"] = "temporal" if args.time_block > 1 else cfg["map"]
+    if args.tile_rows is not None:
+        cfg["tile_rows"] = args.tile_rows
+
+    # ---------------- headline: 4096^2, 1000 sweeps per step -----------------
+    c = inputs.cfg2(dtype)
+    nx, ny, sweeps = c["nx"], c["ny"], c["steps"]
+    u = torch.from_numpy(c["u"]).cuda()
+    v = torch.from_numpy(c["v"]).cuda()
+    stream = torch.cuda.current_stream()
+    launches = binding.stencil_diffuse2d_launches(sweeps, cfg["map"], cfg["time_block"])
+
+    def step():
+        binding.stencil_diffuse2d(u, v, nx, c["alpha"], sweeps, cfg["map"], cfg["time_block"],
+                                  cfg["tile_rows"], stream)
+
+    log(f"headline {nx}x{ny} {args.dtype} {sweeps} sweeps/step, {cfg}, {launches} launches/step")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_s = e0.elapsed_time(e1) / 1e3
+    updates = (nx - 2) * (ny - 2) * sweeps * args.steps
+    value = updates / gpu_s
+    ms_per_step = gpu_s / args.steps * 1e3
+    log(f"headline: {ms_per_step:.3f} ms/step (host clock {wall / args.steps * 1e3:.3f}), "
+        f"{value:.4e} cell-updates/s")
+
+    # roofline of the marching kernel: every launch moves one read of the grid
+    # and one write of its interior; its arithmetic is 7 ops per interior cell
+    # per fused sweep.
+    n_launch = launches * args.steps
+    avg_launch_s = gpu_s / n_launch
+    bytes_per_launch = (nx * ny + (nx - 2) * (ny - 2)) * es
+    sweeps_per_launch = sweeps / launches
+    hbm_gbs = bytes_per_launch / avg_launch_s / 1e9
+    alu_tops = FLOPS_PER_UPDATE * (nx - 2) * (ny - 2) * sweeps_per_launch / avg_launch_s / 1e12
+    hbm_frac, alu_frac = hbm_gbs / HBM_PEAK_GBS, alu_tops / ALU_PEAK_TOPS
+    traffic = None
+    if PROFILE_COUNTERS.exists():
+        prof = json.loads(PROFILE_COUNTERS.read_text())
+        src = ROOT / "structured_grid_cfd_amd" / "csrc" / "diffuse2d.hip"
+        key = f"{args.dtype}_T{cfg['time_block']}"
+        if prof.get("source_sha") == source_hash(src) and key in prof.get("per_launch_bytes", {}):
+            traffic = prof["per_launch_bytes"][key]
+    kernel_name = "k_march<%s, TS=%g>" % ("double" if es == 8 else "float", sweeps_per_launch)
+    if hbm_frac >= alu_frac:
+        roofline = {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(hbm_frac, 4), "traffic": traffic}
+    else:
+        roofline = {"bound": "alu", "achieved": round(alu_tops, 2), "peak": round(ALU_PEAK_TOPS, 2),
+                    "unit": "TFLOP/s", "frac": round(alu_frac, 4), "traffic": traffic}
+    roofline.update({"kernel": kernel_name, "avg_launch_us": round(avg_launch_s * 1e6, 3),
+                     "launches_timed": n_launch, "bytes_per_launch": bytes_per_launch,
+                     "hbm_gbs": round(hbm_gbs, 1), "hbm_frac": round(hbm_frac, 4),
+                     "alu_tflops": round(alu_tops, 2), "alu_frac": round(alu_frac, 4)})
+
+    # ---------------- CPU oracle baseline (bounded sample) ------------------
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        uc, vc = c["u"].copy(), c["v"].copy()
+        log(f"cpu baseline: oracle, {args.cpu_steps} sweeps of the same grid, one thread")
+        t = time.perf_counter()
+        oracle.diffuse2d(uc, vc, nx, c["alpha"], args.cpu_steps)
+        dt = time.perf_counter() - t
+        cpu = {"value": (nx - 2) * (ny - 2) * args.cpu_steps / dt, "unit": "cell-var updates/s",
+               "cores": 1, "kind": "oracle",
+               "sample": f"{nx}x{ny} {args.dtype}, {args.cpu_steps} of the {sweeps} sweeps, "
+                         f"single-threaded C oracle ({dt:.1f} s on {platform.processor() or 'host'}"
+                         f", {os.cpu_count()} host cores visible)"}
+        log(f"cpu baseline: {cpu['value']:.4e} cell-updates/s in {dt:.1f} s")
+
+    kernels = None
+    if not args.quick:
+        del u, v
+        torch.cuda.empty_cache()
+        kernels = measure_all(log)
+
+    line = {
+        "metric": METRIC, "value": value, "unit": "cell-var updates/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": args.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"2D five-point diffusion {nx}x{ny} {args.dtype.upper()}, "
+                               f"{sweeps} sweeps per step, alpha 0.1, zero edges, interior "
+                               f"uniform [0,1) seed 1002",
+                   "map": cfg["map"], "time_block": cfg["time_block"],
+                   "tile_rows": cfg["tile_rows"], "launches_per_step": launches,
+                   "parallelism": "single GPU"},
+        "achieved_hbm_gbs_minimal": round(hbm_gbs, 1),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+    }
+    print(json.dumps(line), flush=True)
+
+
+# ---------------------------------------------------------------------------
+# Per-kernel table (secondary figures; the JSON line's `kernels` object)
+# ---------------------------------------------------------------------------
+
+def measure_all(log) -> dict:
+    import torch
+
+    from structured_grid_cfd_amd import binding, inputs, launch_config
+
+    stream = torch.cuda.current_stream()
+    flush_buf = torch.empty(256 * 1024 * 1024, dtype=torch.float32, device="cuda")  # 1 GiB
+
+    def flush():
+        flush_buf.zero_()  # evicts the 256 MB MALL and the L2s
+
+    def timed(fn, reps, do_flush):
+        out = []
+        for _ in range(reps):
+            if do_flush:
+                flush()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            out.append(e0.elapsed_time(e1) / 1e3)
+        return out
+
+    def entry(times, work, nbytes, extra=None):
+        med = statistics.median(times)
+        d = {"ms": round(med * 1e3, 4), "ms_min": round(min(times) * 1e3, 4),
+             "cellvar_per_s": float("%.4e" % (work / med)),
+             "gbs_minimal": round(nbytes / med / 1e9, 1),
+             "hbm_frac": round(nbytes / med / 1e9 / HBM_PEAK_GBS, 4)}
+        if extra:
+            d.update(extra)
+        return d
+
+    res = {}
+    dev = lambda a: torch.from_numpy(a).cuda()  # noqa: E731
+
+    # reference: a 16-byte-vector copy of 1 GiB (the x pack of one variable)
+    n = 128 * 1024 * 1024
+    src = torch.empty((1, 1, 1, n), dtype=torch.float64, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    binding.field_pack(src, 0, out=dst)
+    t = timed(lambda: binding.field_pack(src, 0, out=dst), 5, True)
+    res["copy_1GiB_dwordx4"] = entry(t, n, 2 * n * 8)
+    log("copy", res["copy_1GiB_dwordx4"])
+    del src, dst
+
+    # diffusion, 4096^2: production in both precisions, the page layouts, time blocks
+    for dt_name, dt in (("f64", np.float64), ("f32", np.float32)):
+        es = 8 if dt_name == "f64" else 4
+        c = inputs.cfg2(dt)
+        nx, ny = c["nx"], c["ny"]
+        per_sweep = (nx * ny + (nx - 2) * (ny - 2)) * es
+        u0, v0 = dev(c["u"]), dev(c["v"])
+        u, v = u0.clone(), v0.clone()
+        cells = (nx - 2) * (ny - 2)
+
+        def run(m, tb, sweeps, rows=0):
+            binding.stencil_diffuse2d(u, v, nx, 0.1, sweeps, m, tb, rows, stream)
+
+        cfg = launch_config.diffusion(dt_name)
+        run(cfg["map"], cfg["time_block"], 1000, cfg["tile_rows"])
+        t = timed(lambda: run(cfg["map"], cfg["time_block"], 1000, cfg["tile_rows"]), 3, False)
+        L = binding.stencil_diffuse2d_launches(1000, cfg["map"], cfg["time_block"])
+        res[f"diffusion_4096_{dt_name}_1000sweeps_production"] = entry(
+            t, cells * 1000, per_sweep * L,
+            {"map": cfg["map"], "time_block": cfg["time_block"], "launches": L,
+             "note": "gbs_minimal counts one grid read + write per launch"})
+        log(dt_name, "production", res[f"diffusion_4096_{dt_name}_1000sweeps_production"])
+        for m in ("collapse_branch", "contig", "strided", "tiled"):
+            sw = 100
+            run(m, 1, 2)
+            t = timed(lambda: run(m, 1, sw), 3, False)
+            res[f"diffusion_4096_{dt_name}_{m}"] = entry(t, cells * sw, per_sweep * sw,
+                                                         {"sweeps": sw})
+            log(dt_name, m, res[f"diffusion_4096_{dt_name}_{m}"])
+        for tb in (2, 3, 4, 6, 8, 10, 12):
+            sw = 240
+            run("temporal", tb, sw)
+            t = timed(lambda: run("temporal", tb, sw), 3, False)
+            L = binding.stencil_diffuse2d_launches(sw, "temporal", tb)
+            res[f"diffusion_4096_{dt_name}_temporal_T{tb}"] = entry(
+                t, cells * sw, per_sweep * L, {"sweeps": sw, "launches": L})
+            log(dt_name, "T", tb, res[f"diffusion_4096_{dt_name}_temporal_T{tb}"])
+        del u, v, u0, v0
+        torch.cuda.empty_cache()
+
+    # 64x64 impulse, 32 sweeps: launch/latency bound
+    c = inputs.cfg1()
+    u, v = dev(c["u"]), dev(c["v"])
+    cfg = launch_config.diffusion("f64")
+    t = timed(lambda: binding.stencil_diffuse2d(u, v, 64, 0.1, 32, cfg["map"], cfg["time_block"],
+                                                0, stream), 10, False)
+    res["diffusion_64_f64_32sweeps"] = entry(t, 62 * 62 * 32, (64 * 64 + 62 * 62) * 8 *
+                                             binding.stencil_diffuse2d_launches(32, cfg["map"], cfg["time_block"]))
+
+    # 16384^2 FP32, 200 sweeps
+    c = inputs.cfg5_diffusion()
+    u, v = dev(c["u"]), dev(c["v"])
+    del c
+    cfg = launch_config.diffusion("f32")
+    nx = ny = 16384
+    binding.stencil_diffuse2d(u, v, nx, 0.1, 8, cfg["map"], cfg["time_block"], 0, stream)
+    t = timed(lambda: binding.stencil_diffuse2d(u, v, nx, 0.1, 200, cfg["map"], cfg["time_block"],
+                                                cfg["tile_rows"], stream), 2, False)
+    L = binding.stencil_diffuse2d_launches(200, cfg["map"], cfg["time_block"])
+    res["diffusion_16384_f32_200sweeps_production"] = entry(
+        t, (nx - 2) * (ny - 2) * 200, (nx * ny + (nx - 2) * (ny - 2)) * 4 * L,
+        {"launches": L, "time_block": cfg["time_block"]})
+    log("16384", res["diffusion_16384_f32_200sweeps_production"])
+    t = timed(lambda: binding.stencil_diffuse2d(u, v, nx, 0.1, 10, "tiled", 1, 0, stream), 2, False)
+    res["diffusion_16384_f32_tiled_single_sweep"] = entry(
+        t, (nx - 2) * (ny - 2) * 10, (nx * ny + (nx - 2) * (ny - 2)) * 4 * 10, {"sweeps": 10})
+    log("16384 tiled", res["diffusion_16384_f32_tiled_single_sweep"])
+    del u, v
+    torch.cuda.empty_cache()
+
+    # pack, 8 x 201^3
+    f = dev(inputs.cfg3())
+    nvar, nz, ny_, nx_ = f.shape
+    cv = nvar * nx_ * ny_ * nz
+    out = torch.empty(cv, dtype=torch.float64, device="cuda")
+    for d, dn in enumerate("xyz"):
+        for m in ("tiled", "per_cell", "per_cellvar"):
+            binding.field_pack(f, d, out=out, map=m)
+            t = timed(lambda: binding.field_pack(f, d, out=out, map=m), 5, True)
+            res[f"pack_201cubed_x8_{dn}_{m}"] = entry(t, cv, 16 * cv)
+            log("pack", dn, m, res[f"pack_201cubed_x8_{dn}_{m}"])
+    del f, out
+    torch.cuda.empty_cache()
+
+    # flux difference, 7 x 201x101x101
+    fi = inputs.cfg4()
+    args = (dev(fi.fx), dev(fi.fy), dev(fi.fz), dev(fi.dx), dev(fi.dy), dev(fi.dz))
+    nvar, nxc, nyc, nzc = fi.shape
+    cv = nvar * nxc * nyc * nzc
+    nbytes = 8 * (fi.fx.size + fi.fy.size + fi.fz.size + cv + nxc + nyc + nzc)
+    rhs = torch.empty(cv, dtype=torch.float64, device="cuda").view(nvar, nzc, nyc, nxc)
+    for m in ("tiled", "per_cell", "per_cellvar"):
+        binding.flux_diff3d(*args, rhs=rhs, map=m)
+        t = timed(lambda: binding.flux_diff3d(*args, rhs=rhs, map=m), 5, True)
+        res[f"flux_201x101x101_x7_{m}"] = entry(t, cv, nbytes)
+        log("flux", m, res[f"flux_201x101x101_x7_{m}"])
+    del args, rhs
+    torch.cuda.empty_cache()
+
+    # 2D workload, 6 x 4800x1200: flux difference and packs along x, y
+    fi = inputs.cfg5_flux()
+    args = (dev(fi.fx), dev(fi.fy), None, dev(fi.dx), dev(fi.dy), None)
+    nvar, nxc, nyc, _ = fi.shape
+    cv = nvar * nxc * nyc
+    nbytes = 8 * (fi.fx.size + fi.fy.size + cv + nxc + nyc)
+    rhs = torch.empty(cv, dtype=torch.float64, device="cuda").view(nvar, 1, nyc, nxc)
+    for m in ("tiled", "per_cell", "per_cellvar"):
+        binding.flux_diff3d(*args, rhs=rhs, map=m)
+        t = timed(lambda: binding.flux_diff3d(*args, rhs=rhs, map=m), 5, True)
+        res[f"flux2d_4800x1200_x6_{m}"] = entry(t, cv, nbytes)
+        log("flux2d", m, res[f"flux2d_4800x1200_x6_{m}"])
+    del args, rhs
+    f = dev(inputs.cfg5_fields())
+    out = torch.empty(cv, dtype=torch.float64, device="cuda")
+    for d, dn in ((0, "x"), (1, "y")):
+        for m in ("tiled", "per_cell", "per_cellvar"):
+            binding.field_pack(f, d, out=out, map=m)
+            t = timed(lambda: binding.field_pack(f, d, out=out, map=m), 5, True)
+            res[f"pack2d_4800x1200_x6_{dn}_{m}"] = entry(t, cv, 16 * cv)
+            log("pack2d", dn, m, res[f"pack2d_4800x1200_x6_{dn}_{m}"])
+    del f, out, flush_buf
+    torch.cuda.empty_cache()
+    return res
+
+
+if __name__ == "__main__":
+    main()

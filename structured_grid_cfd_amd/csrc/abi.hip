@@ -1,0 +1,269 @@
+// abi.hip -- the extern "C" entry points of libsgc.so (include/sgc.h):
+// argument validation on the host before any enqueue, then dispatch to the
+// HIP kernel launchers.  Allocates nothing and keeps no pointers.
+#include <cmath>
+#include <cstdio>
+#include <string>
+
+#include "sgc_internal.h"
+
+namespace sgc {
+
+namespace {
+thread_local std::string g_last_error;
+
+constexpr int64_t kMaxElems = 2147483647LL;  // 32-bit element indices in kernels
+
+bool misaligned(const void *p, int64_t elem_bytes) {
+    return (reinterpret_cast<uintptr_t>(p) % (uintptr_t)elem_bytes) != 0;
+}
+
+bool overlaps(const void *a, int64_t abytes, const void *b, int64_t bbytes) {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
+}
+
+std::string fmt(const char *f, long long x) {
+    char buf[256];
+    std::snprintf(buf, sizeof buf, f, x);
+    return buf;
+}
+
+int clear() {
+    g_last_error.clear();
+    return SGC_OK;
+}
+
+// Number of kernel launches, and the steps each fuses, for a TEMPORAL call:
+// L = ceil(steps / T), bumped by one when its parity differs from the step
+// count's, so that alternating launches u->v, v->u, ... end in v exactly when
+// `steps` is odd; the steps are then spread as evenly as possible (each
+// launch fuses at most T).  L never exceeds `steps`.
+int64_t temporal_launches(int64_t steps, int64_t tb) {
+    if (steps == 0) return 0;
+    int64_t L = (steps + tb - 1) / tb;
+    if ((L & 1) != (steps & 1)) L += 1;
+    return L;
+}
+}  // namespace
+
+int fail(int code, const std::string &msg) {
+    g_last_error = msg;
+    return code;
+}
+
+int check_launch(const char *what) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return fail(SGC_EHIP, std::string(what) + ": " + hipGetErrorString(e));
+    return SGC_OK;
+}
+
+}  // namespace sgc
+
+using namespace sgc;
+
+namespace {
+
+int check_dims(const char *fn, int32_t nvar, int64_t nx, int64_t ny, int64_t nz) {
+    if (nvar < 1 || nvar > SGC_MAX_NVAR)
+        return fail(SGC_EINVAL, std::string(fn) + fmt(": nvar must be in 1..%lld", SGC_MAX_NVAR));
+    if (nx < 1 || ny < 1 || nz < 1) return fail(SGC_EINVAL, std::string(fn) + ": nx, ny, nz must be >= 1");
+    if (nx >= kMaxElems || ny >= kMaxElems || nz >= kMaxElems)
+        return fail(SGC_ERANGE, std::string(fn) + ": an extent exceeds 2^31-2");
+    return SGC_OK;
+}
+
+int check_table(const char *fn, const char *name, const double *const *tab, int32_t nvar) {
+    if (tab == nullptr) return fail(SGC_ENULL, std::string(fn) + ": " + name + " table is NULL");
+    for (int32_t k = 0; k < nvar; ++k) {
+        if (tab[k] == nullptr)
+            return fail(SGC_ENULL, std::string(fn) + ": " + name + fmt(" entry %lld is NULL", k));
+        if (misaligned(tab[k], 8))
+            return fail(SGC_EINVAL, std::string(fn) + ": " + name + fmt(" entry %lld is not 8-byte aligned", k));
+    }
+    return SGC_OK;
+}
+
+int check_ptr(const char *fn, const char *name, const double *p) {
+    if (p == nullptr) return fail(SGC_ENULL, std::string(fn) + ": " + name + " is NULL");
+    if (misaligned(p, 8)) return fail(SGC_EINVAL, std::string(fn) + ": " + name + " is not 8-byte aligned");
+    return SGC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *sgc_last_error(void) { return g_last_error.c_str(); }
+
+int32_t sgc_abi_version(void) { return SGC_ABI_VERSION; }
+
+int64_t stencil_diffuse2d_launches(int64_t steps, int32_t map, int32_t time_block) {
+    if (steps < 0) return -1;
+    switch (map) {
+    case SGC_DIFF_COLLAPSE_BRANCH:
+    case SGC_DIFF_CONTIG:
+    case SGC_DIFF_STRIDED:
+    case SGC_DIFF_TILED:
+        return steps;
+    case SGC_DIFF_TEMPORAL:
+        if (time_block < 1 || time_block > SGC_MAX_TIME_BLOCK) return -1;
+        return temporal_launches(steps, time_block);
+    default:
+        return -1;
+    }
+}
+
+int stencil_diffuse2d(void *u, void *v, int32_t dtype, int64_t nx, int64_t ny, int64_t ld,
+                      double alpha, int64_t steps, int32_t map, int32_t time_block,
+                      int32_t tile_rows, void *stream, int32_t *result_is_v) {
+    clear();
+    if (u == nullptr || v == nullptr) return fail(SGC_ENULL, "stencil_diffuse2d: u and v must be non-NULL");
+    if (dtype != SGC_F32 && dtype != SGC_F64)
+        return fail(SGC_EDTYPE, fmt("stencil_diffuse2d: unknown dtype %lld", dtype));
+    if (nx < 3 || ny < 3) return fail(SGC_EINVAL, "stencil_diffuse2d: nx and ny must be >= 3");
+    if (ld < nx) return fail(SGC_EINVAL, "stencil_diffuse2d: ld must be >= nx");
+    if (steps < 0) return fail(SGC_EINVAL, "stencil_diffuse2d: steps must be >= 0");
+    if (!std::isfinite(alpha)) return fail(SGC_EINVAL, "stencil_diffuse2d: alpha must be finite");
+    if (map < SGC_DIFF_COLLAPSE_BRANCH || map > SGC_DIFF_TEMPORAL)
+        return fail(SGC_EINVAL, fmt("stencil_diffuse2d: unknown map %lld", map));
+    if (map == SGC_DIFF_TEMPORAL) {
+        if (time_block < 1) return fail(SGC_EINVAL, "stencil_diffuse2d: time_block must be >= 1");
+        if (time_block > SGC_MAX_TIME_BLOCK)
+            return fail(SGC_ERANGE, fmt("stencil_diffuse2d: time_block above %lld", SGC_MAX_TIME_BLOCK));
+    }
+    if (map == SGC_DIFF_TILED || map == SGC_DIFF_TEMPORAL) {
+        if (tile_rows < 0 || tile_rows > ny)
+            return fail(SGC_EINVAL, "stencil_diffuse2d: tile_rows must be 0 (auto) or 1..ny");
+    }
+    if (ld > kMaxElems / ny) return fail(SGC_ERANGE, "stencil_diffuse2d: ld*ny exceeds 2^31-1 elements");
+    const int64_t es = dtype == SGC_F64 ? 8 : 4;
+    const int64_t bytes = ld * ny * es;
+    if (misaligned(u, es) || misaligned(v, es))
+        return fail(SGC_EINVAL, "stencil_diffuse2d: u and v must be aligned to their element size");
+    if (overlaps(u, bytes, v, bytes)) return fail(SGC_EALIAS, "stencil_diffuse2d: u and v overlap");
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    DiffPlan p{(int)nx, (int)ny, (int)ld, time_block, tile_rows};
+    int rc = SGC_OK;
+    if (steps == 0) {
+        rc = diffuse_zero_ring(u, dtype, p.nx, p.ny, p.ld, s);
+        if (rc) return rc;
+    } else if (map == SGC_DIFF_COLLAPSE_BRANCH || map == SGC_DIFF_CONTIG || map == SGC_DIFF_STRIDED) {
+        // The page layouts read the edge ring as the Dirichlet value: start
+        // from zero rings in both buffers, as the pages' initial condition does.
+        if ((rc = diffuse_zero_ring(u, dtype, p.nx, p.ny, p.ld, s))) return rc;
+        if ((rc = diffuse_zero_ring(v, dtype, p.nx, p.ny, p.ld, s))) return rc;
+        for (int64_t k = 1; k <= steps; ++k) {
+            const bool odd = (k & 1) != 0;
+            rc = diffuse_sweep(odd ? u : v, odd ? v : u, dtype, p, alpha, map, 1, s);
+            if (rc) return rc;
+        }
+    } else if (map == SGC_DIFF_TILED) {
+        // The march treats the ring as 0 on read and writes it as 0.
+        for (int64_t k = 1; k <= steps; ++k) {
+            const bool odd = (k & 1) != 0;
+            rc = diffuse_sweep(odd ? u : v, odd ? v : u, dtype, p, alpha, map, 1, s);
+            if (rc) return rc;
+        }
+    } else {  // TEMPORAL
+        const int64_t L = temporal_launches(steps, time_block);
+        const int64_t base = steps / L, extra = steps % L;
+        for (int64_t k = 0; k < L; ++k) {
+            const int ts = (int)(base + (k < extra ? 1 : 0));
+            const bool fwd = (k & 1) == 0;
+            rc = diffuse_sweep(fwd ? u : v, fwd ? v : u, dtype, p, alpha, map, ts, s);
+            if (rc) return rc;
+        }
+    }
+    if (result_is_v) *result_is_v = (int32_t)(steps & 1);
+    return SGC_OK;
+}
+
+int field_pack(const double *const *fields, int32_t nvar, int64_t nx, int64_t ny, int64_t nz,
+               int32_t dir, double *out, int32_t map, void *stream) {
+    clear();
+    int rc;
+    if ((rc = check_dims("field_pack", nvar, nx, ny, nz))) return rc;
+    if ((rc = check_table("field_pack", "fields", fields, nvar))) return rc;
+    if ((rc = check_ptr("field_pack", "out", out))) return rc;
+    if (dir < SGC_DIR_X || dir > SGC_DIR_Z) return fail(SGC_EINVAL, "field_pack: dir must be 0, 1 or 2");
+    if (map < SGC_VAR_PER_CELL || map > SGC_VAR_TILED) return fail(SGC_EINVAL, "field_pack: unknown map");
+    if (nx * ny > kMaxElems / nz || nx * ny * nz > kMaxElems / nvar)
+        return fail(SGC_ERANGE, "field_pack: nvar*nx*ny*nz exceeds 2^31-1 elements");
+    const int64_t n = nx * ny * nz;
+    for (int32_t k = 0; k < nvar; ++k)
+        if (overlaps(out, n * nvar * 8, fields[k], n * 8))
+            return fail(SGC_EALIAS, fmt("field_pack: out overlaps field %lld", k));
+    PtrTable t{};
+    for (int32_t k = 0; k < nvar; ++k) t.p[k] = fields[k];
+    return pack_launch(t, nvar, (int)nx, (int)ny, (int)nz, dir, out, map, static_cast<hipStream_t>(stream));
+}
+
+int field_unpack(const double *packed, int32_t nvar, int64_t nx, int64_t ny, int64_t nz, int32_t dir,
+                 double *const *fields, int32_t map, void *stream) {
+    clear();
+    int rc;
+    if ((rc = check_dims("field_unpack", nvar, nx, ny, nz))) return rc;
+    if ((rc = check_ptr("field_unpack", "packed", packed))) return rc;
+    if ((rc = check_table("field_unpack", "fields", fields, nvar))) return rc;
+    if (dir < SGC_DIR_X || dir > SGC_DIR_Z) return fail(SGC_EINVAL, "field_unpack: dir must be 0, 1 or 2");
+    if (map < SGC_VAR_PER_CELL || map > SGC_VAR_TILED) return fail(SGC_EINVAL, "field_unpack: unknown map");
+    if (nx * ny > kMaxElems / nz || nx * ny * nz > kMaxElems / nvar)
+        return fail(SGC_ERANGE, "field_unpack: nvar*nx*ny*nz exceeds 2^31-1 elements");
+    const int64_t n = nx * ny * nz;
+    for (int32_t k = 0; k < nvar; ++k) {
+        if (overlaps(packed, n * nvar * 8, fields[k], n * 8))
+            return fail(SGC_EALIAS, fmt("field_unpack: field %lld overlaps packed", k));
+        for (int32_t m = 0; m < k; ++m)
+            if (overlaps(fields[m], n * 8, fields[k], n * 8))
+                return fail(SGC_EALIAS, fmt("field_unpack: field %lld overlaps an earlier field", k));
+    }
+    PtrTable t{};
+    for (int32_t k = 0; k < nvar; ++k) t.p[k] = fields[k];
+    return unpack_launch(packed, nvar, (int)nx, (int)ny, (int)nz, dir, t, map,
+                         static_cast<hipStream_t>(stream));
+}
+
+int flux_diff3d(const double *const *fx, const double *const *fy, const double *const *fz,
+                const double *dx, const double *dy, const double *dz, int32_t nvar, int64_t nx,
+                int64_t ny, int64_t nz, double *rhs, int32_t map, void *stream) {
+    clear();
+    int rc;
+    if ((rc = check_dims("flux_diff3d", nvar, nx, ny, nz))) return rc;
+    if ((rc = check_table("flux_diff3d", "fx", fx, nvar))) return rc;
+    if ((rc = check_table("flux_diff3d", "fy", fy, nvar))) return rc;
+    if (fz != nullptr && (rc = check_table("flux_diff3d", "fz", fz, nvar))) return rc;
+    if ((rc = check_ptr("flux_diff3d", "dx", dx))) return rc;
+    if ((rc = check_ptr("flux_diff3d", "dy", dy))) return rc;
+    if ((fz == nullptr) != (dz == nullptr))
+        return fail(SGC_ENULL, "flux_diff3d: fz and dz must both be given or both be NULL");
+    if (dz != nullptr && (rc = check_ptr("flux_diff3d", "dz", dz))) return rc;
+    if (fz == nullptr && nz != 1) return fail(SGC_EINVAL, "flux_diff3d: the 2D form (fz NULL) needs nz == 1");
+    if ((rc = check_ptr("flux_diff3d", "rhs", rhs))) return rc;
+    if (map < SGC_VAR_PER_CELL || map > SGC_VAR_TILED) return fail(SGC_EINVAL, "flux_diff3d: unknown map");
+    const int64_t nfx = (nx + 1) * ny * nz, nfy = nx * (ny + 1) * nz, nfz = nx * ny * (nz + 1);
+    const int64_t n = nx * ny * nz;
+    if ((nx + 1) * (ny + 1) > kMaxElems / (nz + 1) || n > kMaxElems / nvar)
+        return fail(SGC_ERANGE, "flux_diff3d: an array exceeds 2^31-1 elements");
+    const int64_t rbytes = n * nvar * 8;
+    for (int32_t k = 0; k < nvar; ++k) {
+        if (overlaps(rhs, rbytes, fx[k], nfx * 8)) return fail(SGC_EALIAS, "flux_diff3d: rhs overlaps fx");
+        if (overlaps(rhs, rbytes, fy[k], nfy * 8)) return fail(SGC_EALIAS, "flux_diff3d: rhs overlaps fy");
+        if (fz && overlaps(rhs, rbytes, fz[k], nfz * 8)) return fail(SGC_EALIAS, "flux_diff3d: rhs overlaps fz");
+    }
+    if (overlaps(rhs, rbytes, dx, nx * 8) || overlaps(rhs, rbytes, dy, ny * 8) ||
+        (dz && overlaps(rhs, rbytes, dz, nz * 8)))
+        return fail(SGC_EALIAS, "flux_diff3d: rhs overlaps a spacing array");
+    PtrTable tx{}, ty{}, tz{};
+    for (int32_t k = 0; k < nvar; ++k) {
+        tx.p[k] = fx[k];
+        ty.p[k] = fy[k];
+        if (fz) tz.p[k] = fz[k];
+    }
+    return flux_launch(tx, ty, fz ? &tz : nullptr, dx, dy, dz, nvar, (int)nx, (int)ny, (int)nz, rhs, map,
+                       static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

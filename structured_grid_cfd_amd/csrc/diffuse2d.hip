@@ -1,0 +1,387 @@
+// diffuse2d.hip -- explicit 2D five-point diffusion sweeps for gfx950.
+//
+// Operation (Qiita "Fortran 2018でGPUを高速化する Part 3", section 3):
+//   v(i,j) = u(i,j) + alpha*(u(i-1,j) + u(i+1,j) + u(i,j-1) + u(i,j+1) - 4u(i,j))
+// on interior cells, edges fixed at 0, column-major storage with i contiguous
+// (section 4).  Five thread mappings:
+//   * k_collapse_branch, k_contig, k_strided -- the three loop layouts of
+//     section 5.1-5.3 (flattened grid with an edge branch; workgroup per row
+//     with lanes along i; workgroup per column with lanes along j);
+//   * k_march<T, TS, VEC> -- this library's sweep: one wave owns a strip of
+//     64*K columns (K elements per lane = one 16-byte load) and marches up a
+//     tile of rows, keeping a three-row register window per time level.
+//     West/east neighbours cross lanes with DPP wave shifts, north/south come
+//     from the window, so every input row is read from memory exactly once and
+//     every output row written once per launch.  TS > 1 fuses TS time steps in
+//     one launch (temporal blocking): the strip carries a halo of TS columns on
+//     each side and the tile TS extra rows above and below, recomputed
+//     redundantly, which section 5.4 notes is what a correct fusion across
+//     steps needs.  Every cell of a level is produced by the same expression as
+//     a single step, so all mappings give identical bits.
+#include "sgc_internal.h"
+
+namespace sgc {
+namespace {
+
+// c + a*((((W + E) + S) + N) - 4c): left-to-right sum, one rounding per
+// operation, no fused multiply-add (fused c + a*t would change the bits).
+template <typename T>
+__device__ __forceinline__ T five_point(T w, T e, T s, T n, T c, T a) {
+#pragma clang fp contract(off)
+    T t = w + e;
+    t = t + s;
+    t = t + n;
+    t = t - T(4) * c;
+    return c + a * t;
+}
+
+// ---------------------------------------------------------------------------
+// The pages' three loop layouts
+// ---------------------------------------------------------------------------
+
+// Section 5.1: collapse(2) over all cells; edge cells get 0 through a branch.
+template <typename T>
+__global__ __launch_bounds__(256) void k_collapse_branch(const T *__restrict__ src,
+                                                         T *__restrict__ dst, int nx,
+                                                         int ny, int ld, T a) {
+    const int idx = blockIdx.x * 256 + threadIdx.x;
+    if (idx >= nx * ny) return;
+    const int j = idx / nx;
+    const int i = idx - j * nx;
+    const int p = i + ld * j;
+    T out = T(0);
+    if (!(i == 0 || i == nx - 1 || j == 0 || j == ny - 1))
+        out = five_point(src[p - 1], src[p + 1], src[p - ld], src[p + ld], src[p], a);
+    dst[p] = out;
+}
+
+// Section 5.2: one workgroup per interior row j, lanes along i (contiguous).
+template <typename T>
+__global__ __launch_bounds__(256) void k_contig(const T *__restrict__ src, T *__restrict__ dst,
+                                                int nx, int ny, int ld, T a) {
+    const int j = 1 + blockIdx.x;
+    for (int i = 1 + threadIdx.x; i < nx - 1; i += 256) {
+        const int p = i + ld * j;
+        dst[p] = five_point(src[p - 1], src[p + 1], src[p - ld], src[p + ld], src[p], a);
+    }
+}
+
+// Section 5.3: one workgroup per interior column i, lanes along j (stride ld).
+template <typename T>
+__global__ __launch_bounds__(256) void k_strided(const T *__restrict__ src, T *__restrict__ dst,
+                                                 int nx, int ny, int ld, T a) {
+    const int i = 1 + blockIdx.x;
+    for (int j = 1 + threadIdx.x; j < ny - 1; j += 256) {
+        const int p = i + ld * j;
+        dst[p] = five_point(src[p - 1], src[p + 1], src[p - ld], src[p + ld], src[p], a);
+    }
+}
+
+// Zero the edge ring (rows 0 and ny-1, columns 0 and nx-1) of one buffer.
+template <typename T>
+__global__ __launch_bounds__(256) void k_zero_ring(T *__restrict__ g, int nx, int ny, int ld) {
+    const int t = blockIdx.x * 256 + threadIdx.x;
+    if (t < nx)
+        g[t] = T(0);
+    else if (t < 2 * nx)
+        g[(t - nx) + ld * (ny - 1)] = T(0);
+    else if (t < 2 * nx + ny)
+        g[ld * (t - 2 * nx)] = T(0);
+    else if (t < 2 * nx + 2 * ny)
+        g[(nx - 1) + ld * (t - 2 * nx - ny)] = T(0);
+}
+
+// ---------------------------------------------------------------------------
+// Marching strip sweep with optional temporal blocking
+// ---------------------------------------------------------------------------
+
+template <typename T> struct LaneVec;
+template <> struct LaneVec<float> {
+    static constexpr int K = 4;
+    typedef float type __attribute__((ext_vector_type(4)));
+};
+template <> struct LaneVec<double> {
+    static constexpr int K = 2;
+    typedef double type __attribute__((ext_vector_type(2)));
+};
+
+// DPP wavefront shifts by one lane (GFX9 dpp_ctrl 0x138 wave_shr:1 and 0x130
+// wave_shl:1).  shr: lane l receives lane l-1's value; shl: lane l receives
+// lane l+1's.  Lanes without a source keep 0; they only ever feed the halo
+// columns that the march discards.
+__device__ __forceinline__ float wave_shr1(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x138, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float wave_shl1(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x130, 0xf, 0xf, false));
+}
+__device__ __forceinline__ double wave_shr1(double x) {
+    const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(x), 0x138, 0xf, 0xf, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(x), 0x138, 0xf, 0xf, false);
+    return __hiloint2double(hi, lo);
+}
+__device__ __forceinline__ double wave_shl1(double x) {
+    const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(x), 0x130, 0xf, 0xf, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(x), 0x130, 0xf, 0xf, false);
+    return __hiloint2double(hi, lo);
+}
+
+struct MarchArgs {
+    const void *src;
+    void *dst;
+    int nx, ny, ld;
+    int nstrips;    // strips across the grid (OW output columns each)
+    int ntiles;     // nstrips * row tiles
+    int tile_rows;  // output rows per tile
+    double alpha;
+};
+
+template <typename T> constexpr int march_halo(int ts) {
+    return ((ts + LaneVec<T>::K - 1) / LaneVec<T>::K) * LaneVec<T>::K;
+}
+template <typename T> constexpr int march_out_width(int ts) {
+    return 64 * LaneVec<T>::K - 2 * march_halo<T>(ts);
+}
+
+// One wave's march.  EDGE: the strip touches the first/last column or runs
+// past the grid, so per-element column masks are needed; interior strips
+// skip them.  VEC: 16-byte aligned rows, one vector load/store per lane-row.
+template <typename T, int TS, bool VEC, bool EDGE>
+__device__ __forceinline__ void march(const T *__restrict__ src, T *__restrict__ dst, int nx,
+                                      int ny, int ld, T a, int lane, int col_out0,
+                                      int row_out0, int row_out1) {
+    constexpr int K = LaneVec<T>::K;
+    constexpr int HALO = march_halo<T>(TS);
+    constexpr int OW = march_out_width<T>(TS);
+    typedef typename LaneVec<T>::type V;
+
+    const int c0 = col_out0 - HALO + lane * K;  // first column this lane holds
+    bool colin[K];                              // column is an interior column
+#pragma unroll
+    for (int e = 0; e < K; ++e) colin[e] = EDGE ? (c0 + e >= 1 && c0 + e <= nx - 2) : true;
+    const bool lane_out = c0 >= col_out0 && c0 < col_out0 + OW;
+
+    const int r_first = row_out0 - TS;        // first input row of the march
+    const int nit = row_out1 - row_out0 + 2 * TS;
+    const int nit3 = ((nit + 2) / 3) * 3;     // three-phase unrolled loop
+    const int r_load_max = min(ny - 2, row_out1 - 1 + TS);
+
+    T win[TS][3][K];  // win[s][slot][e]: level-s rows, slot = row phase mod 3
+    T pre[3][K];      // level-0 rows in flight, three rows ahead
+#pragma unroll
+    for (int s = 0; s < TS; ++s)
+#pragma unroll
+        for (int p = 0; p < 3; ++p)
+#pragma unroll
+            for (int e = 0; e < K; ++e) win[s][p][e] = T(0);
+
+    auto load_row = [&](T (&x)[K], int r) {
+        if (r >= 1 && r <= r_load_max) {  // only interior rows are non-zero
+            const T *rowp = src + r * ld + c0;
+            if (VEC) {
+                V y = V(T(0));
+                if (!EDGE || (c0 >= 0 && c0 < nx)) y = *reinterpret_cast<const V *>(rowp);
+#pragma unroll
+                for (int e = 0; e < K; ++e) x[e] = colin[e] ? y[e] : T(0);
+            } else {
+#pragma unroll
+                for (int e = 0; e < K; ++e) x[e] = colin[e] ? rowp[e] : T(0);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < K; ++e) x[e] = T(0);
+        }
+    };
+
+    auto store_row = [&](const T (&x)[K], int q) {
+        T *rowp = dst + q * ld + c0;
+        if (VEC && (!EDGE || c0 + K <= nx)) {
+            V y;
+#pragma unroll
+            for (int e = 0; e < K; ++e) y[e] = x[e];
+            *reinterpret_cast<V *>(rowp) = y;
+        } else {
+#pragma unroll
+            for (int e = 0; e < K; ++e)
+                if (!EDGE || c0 + e < nx) rowp[e] = x[e];
+        }
+    };
+
+#pragma unroll
+    for (int p = 0; p < 3; ++p) load_row(pre[p], r_first + p);
+
+    auto step = [&](auto phase, int it) {
+        constexpr int P = decltype(phase)::value;
+        constexpr int PC = (P + 2) % 3;  // previous row (centre for the next level)
+        constexpr int PS = (P + 1) % 3;  // row before that (south)
+        const int r = r_first + it;
+#pragma unroll
+        for (int e = 0; e < K; ++e) win[0][P][e] = pre[P][e];
+        load_row(pre[P], r + 3);
+#pragma unroll
+        for (int s = 1; s <= TS; ++s) {
+            if (it >= 2 * s) {  // level s row r-s depends only on loaded rows
+                const int q = r - s;
+                const bool rowin = q >= 1 && q <= ny - 2;
+                const T wl = wave_shr1(win[s - 1][PC][K - 1]);
+                const T er = wave_shl1(win[s - 1][PC][0]);
+                T res[K];
+#pragma unroll
+                for (int e = 0; e < K; ++e) {
+                    const T w = e == 0 ? wl : win[s - 1][PC][e - 1];
+                    const T ee = e == K - 1 ? er : win[s - 1][PC][e + 1];
+                    T val = five_point(w, ee, win[s - 1][PS][e], win[s - 1][P][e],
+                                       win[s - 1][PC][e], a);
+                    if (EDGE && !colin[e]) val = T(0);
+                    res[e] = rowin ? val : T(0);
+                }
+                if (s < TS) {
+#pragma unroll
+                    for (int e = 0; e < K; ++e) win[s < TS ? s : 0][P][e] = res[e];
+                } else if (q >= row_out0 && q < row_out1 && lane_out) {
+                    store_row(res, q);
+                }
+            }
+        }
+    };
+
+    for (int it = 0; it < nit3; it += 3) {
+        step(std::integral_constant<int, 0>{}, it);
+        step(std::integral_constant<int, 1>{}, it + 1);
+        step(std::integral_constant<int, 2>{}, it + 2);
+    }
+}
+
+template <typename T, int TS, bool VEC>
+__global__ __launch_bounds__(256) void k_march(MarchArgs g) {
+    constexpr int K = LaneVec<T>::K;
+    constexpr int HALO = march_halo<T>(TS);
+    constexpr int OW = march_out_width<T>(TS);
+    static_assert(OW > 0, "time block too deep for the strip width");
+    const int lane = threadIdx.x & 63;
+    const int tile = xcd_remap(blockIdx.x, gridDim.x) * 4 + (threadIdx.x >> 6);
+    if (tile >= g.ntiles) return;  // whole wave leaves; the kernel has no barriers
+    const int strip = tile % g.nstrips;
+    const int rtile = tile / g.nstrips;
+    const int col_out0 = strip * OW;
+    const int row_out0 = rtile * g.tile_rows;
+    const int row_out1 = min(row_out0 + g.tile_rows, g.ny);
+    const T *src = static_cast<const T *>(g.src);
+    T *dst = static_cast<T *>(g.dst);
+    const T a = T(g.alpha);
+    const int span0 = col_out0 - HALO;  // first column of the strip
+    const bool interior = span0 >= 1 && span0 + 64 * K <= g.nx - 1;
+    if (interior)
+        march<T, TS, VEC, false>(src, dst, g.nx, g.ny, g.ld, a, lane, col_out0, row_out0, row_out1);
+    else
+        march<T, TS, VEC, true>(src, dst, g.nx, g.ny, g.ld, a, lane, col_out0, row_out0, row_out1);
+}
+
+// ---------------------------------------------------------------------------
+// Host-side launch selection
+// ---------------------------------------------------------------------------
+
+constexpr int kTargetTiles = 4096;  // ~16 waves per CU over 256 CUs
+
+template <typename T> int out_width(int ts) {
+    const int K = LaneVec<T>::K;
+    const int halo = ((ts + K - 1) / K) * K;
+    return 64 * K - 2 * halo;
+}
+
+template <typename T, int TS>
+int launch_march_ts(const void *src, void *dst, const DiffPlan &p, double alpha, hipStream_t s) {
+    MarchArgs g;
+    g.src = src;
+    g.dst = dst;
+    g.nx = p.nx;
+    g.ny = p.ny;
+    g.ld = p.ld;
+    g.alpha = alpha;
+    const int ow = out_width<T>(TS);
+    g.nstrips = (p.nx + ow - 1) / ow;
+    int rows = p.tile_rows;
+    if (rows <= 0) {
+        const int chunks = (kTargetTiles + g.nstrips - 1) / g.nstrips;
+        rows = (p.ny + chunks - 1) / chunks;
+        rows = max(rows, max(16, 4 * TS));
+    }
+    rows = min(rows, p.ny);
+    g.tile_rows = rows;
+    const long ntiles = (long)g.nstrips * ((p.ny + rows - 1) / rows);
+    g.ntiles = (int)ntiles;
+    const int blocks = (int)((ntiles + 3) / 4);
+    const bool vec = (reinterpret_cast<uintptr_t>(src) % 16 == 0) &&
+                     (reinterpret_cast<uintptr_t>(dst) % 16 == 0) &&
+                     ((long)p.ld * (long)sizeof(T)) % 16 == 0;
+    if (vec)
+        hipLaunchKernelGGL((k_march<T, TS, true>), dim3(blocks), dim3(256), 0, s, g);
+    else
+        hipLaunchKernelGGL((k_march<T, TS, false>), dim3(blocks), dim3(256), 0, s, g);
+    return check_launch("diffusion march kernel");
+}
+
+template <typename T>
+int launch_march(const void *src, void *dst, const DiffPlan &p, double alpha, int ts,
+                 hipStream_t s) {
+    switch (ts) {
+#define SGC_TS_CASE(n) \
+    case n: return launch_march_ts<T, n>(src, dst, p, alpha, s);
+        SGC_TS_CASE(1) SGC_TS_CASE(2) SGC_TS_CASE(3) SGC_TS_CASE(4)
+        SGC_TS_CASE(5) SGC_TS_CASE(6) SGC_TS_CASE(7) SGC_TS_CASE(8)
+        SGC_TS_CASE(9) SGC_TS_CASE(10) SGC_TS_CASE(11) SGC_TS_CASE(12)
+#undef SGC_TS_CASE
+    default: return fail(SGC_ERANGE, "time block out of range");
+    }
+}
+static_assert(SGC_MAX_TIME_BLOCK == 12, "launch_march instantiates 1..12");
+
+template <typename T>
+int sweep_t(const void *src, void *dst, const DiffPlan &p, double alpha, int map, int ts,
+            hipStream_t s) {
+    const T *in = static_cast<const T *>(src);
+    T *out = static_cast<T *>(dst);
+    const T a = T(alpha);
+    switch (map) {
+    case SGC_DIFF_COLLAPSE_BRANCH: {
+        const long n = (long)p.nx * p.ny;
+        hipLaunchKernelGGL((k_collapse_branch<T>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                           in, out, p.nx, p.ny, p.ld, a);
+        return check_launch("collapse-branch sweep");
+    }
+    case SGC_DIFF_CONTIG:
+        hipLaunchKernelGGL((k_contig<T>), dim3(p.ny - 2), dim3(256), 0, s, in, out, p.nx, p.ny, p.ld, a);
+        return check_launch("contiguous-lane sweep");
+    case SGC_DIFF_STRIDED:
+        hipLaunchKernelGGL((k_strided<T>), dim3(p.nx - 2), dim3(256), 0, s, in, out, p.nx, p.ny, p.ld, a);
+        return check_launch("strided-lane sweep");
+    case SGC_DIFF_TILED:
+        return launch_march<T>(src, dst, p, alpha, 1, s);
+    case SGC_DIFF_TEMPORAL:
+        return launch_march<T>(src, dst, p, alpha, ts, s);
+    default:
+        return fail(SGC_EINVAL, "unknown diffusion map");
+    }
+}
+
+}  // namespace
+
+int diffuse_zero_ring(void *buf, int dtype, int nx, int ny, int ld, hipStream_t s) {
+    const int n = 2 * nx + 2 * ny;
+    const dim3 grid((n + 255) / 256);
+    if (dtype == SGC_F64)
+        hipLaunchKernelGGL((k_zero_ring<double>), grid, dim3(256), 0, s, static_cast<double *>(buf), nx,
+                           ny, ld);
+    else
+        hipLaunchKernelGGL((k_zero_ring<float>), grid, dim3(256), 0, s, static_cast<float *>(buf), nx,
+                           ny, ld);
+    return check_launch("edge-ring zeroing");
+}
+
+int diffuse_sweep(const void *src, void *dst, int dtype, const DiffPlan &p, double alpha, int map,
+                  int steps_in_launch, hipStream_t s) {
+    if (dtype == SGC_F64) return sweep_t<double>(src, dst, p, alpha, map, steps_in_launch, s);
+    return sweep_t<float>(src, dst, p, alpha, map, steps_in_launch, s);
+}
+
+}  // namespace sgc

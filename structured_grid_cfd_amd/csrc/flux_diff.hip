@@ -1,0 +1,204 @@
+// flux_diff.hip -- conservative flux difference over nvar fields, gfx950.
+//
+// Operation (MFC pull request 2087, "SCC26: Collapse only spatial loops in
+// per-variable GPU kernels", Changes: the x/y/z flux-difference loops, with
+// the inverse grid spacing computed outside the variable loop):
+//   rhs(j,k,l,v) = ((Fx(j)-Fx(j+1))*(1/dx[j]) + (Fy(k)-Fy(k+1))*(1/dy[k]))
+//                  + (Fz(l)-Fz(l+1))*(1/dz[l])
+// with one rounding per operation, no fused multiply-add, and each reciprocal
+// a correctly rounded FP64 division, so every mapping returns the same bits.
+// Three variable mappings:
+//   * PER_CELLVAR -- one thread per (var, cell), index decomposition and the
+//     three reciprocals per thread (the page's "before");
+//   * PER_CELL -- one thread per cell, reciprocals once, variables looped
+//     inside (the page's "after");
+//   * TILED -- one thread per (j, k) column marching a run of l planes: the
+//     high z face of plane l is kept in a register as the low face of plane
+//     l+1, so every face is read from memory once; 1/dx and 1/dy are formed
+//     once per column and 1/dz once per plane per workgroup (in LDS).  The 2D
+//     form marches along k instead, treating Fy as the marched face.
+#include "sgc_internal.h"
+
+namespace sgc {
+namespace {
+
+struct FluxArgs {
+    PtrTable fx, fy, fz;
+    const double *dx, *dy, *dz;
+    double *rhs;
+    int nvar, nx, ny, nz;
+};
+
+__device__ __forceinline__ double face_term(double lo, double hi, double inv) {
+#pragma clang fp contract(off)
+    return (lo - hi) * inv;
+}
+
+__device__ __forceinline__ double add(double a, double b) {
+#pragma clang fp contract(off)
+    return a + b;
+}
+
+// One thread per cell; variables looped inside the thread.
+template <bool HAS_Z>
+__global__ __launch_bounds__(256) void k_flux_per_cell(FluxArgs g) {
+    const int n = g.nx * g.ny * g.nz;
+    const int idx = blockIdx.x * 256 + threadIdx.x;
+    if (idx >= n) return;
+    const int j = idx % g.nx;
+    const int t = idx / g.nx;
+    const int k = t % g.ny;
+    const int l = t / g.ny;
+    const double ix = 1.0 / g.dx[j];
+    const double iy = 1.0 / g.dy[k];
+    const double iz = HAS_Z ? 1.0 / g.dz[l] : 0.0;
+    const int ox = j + (g.nx + 1) * (k + g.ny * l);
+    const int oy = j + g.nx * (k + (g.ny + 1) * l);
+    const int sz = g.nx * g.ny;
+    for (int v = 0; v < g.nvar; ++v) {
+        double r = face_term(g.fx.p[v][ox], g.fx.p[v][ox + 1], ix);
+        r = add(r, face_term(g.fy.p[v][oy], g.fy.p[v][oy + g.nx], iy));
+        if (HAS_Z) r = add(r, face_term(g.fz.p[v][idx], g.fz.p[v][idx + sz], iz));
+        g.rhs[idx + v * n] = r;
+    }
+}
+
+// One thread per (var, cell): everything recomputed per thread.
+template <bool HAS_Z>
+__global__ __launch_bounds__(256) void k_flux_per_cellvar(FluxArgs g) {
+    const int n = g.nx * g.ny * g.nz;
+    const int idx = blockIdx.x * 256 + threadIdx.x;
+    if (idx >= n * g.nvar) return;
+    const int j = idx % g.nx;
+    int t = idx / g.nx;
+    const int k = t % g.ny;
+    t /= g.ny;
+    const int l = t % g.nz;
+    const int v = t / g.nz;
+    const double ix = 1.0 / g.dx[j];
+    const double iy = 1.0 / g.dy[k];
+    const int ox = j + (g.nx + 1) * (k + g.ny * l);
+    const int oy = j + g.nx * (k + (g.ny + 1) * l);
+    const int oc = j + g.nx * (k + g.ny * l);
+    double r = face_term(g.fx.p[v][ox], g.fx.p[v][ox + 1], ix);
+    r = add(r, face_term(g.fy.p[v][oy], g.fy.p[v][oy + g.nx], iy));
+    if (HAS_Z) {
+        const double iz = 1.0 / g.dz[l];
+        r = add(r, face_term(g.fz.p[v][oc], g.fz.p[v][oc + g.nx * g.ny], iz));
+    }
+    g.rhs[oc + v * n] = r;
+}
+
+// Column pencils marching the slowest axis.  View (nxv, nyv, nzv): the 3D
+// form is (nx, ny, nz) with y and z terms; the 2D form is (nx, 1, ny) whose
+// marched face array is Fy and whose widths along the march are dy (there is
+// no separate y term), giving the same sum x + y as the definition.
+constexpr int kMaxPlanes = 256;
+
+struct PencilArgs {
+    FluxArgs g;
+    int nxv, nyv, nzv;
+    int planes;       // planes per workgroup run
+    int col_blocks;   // workgroups across the nxv*nyv columns
+};
+
+template <bool HAS_Y>
+__global__ __launch_bounds__(256) void k_flux_pencil(PencilArgs a) {
+    __shared__ double iz_s[kMaxPlanes];
+    const FluxArgs &g = a.g;
+    const int b = xcd_remap(blockIdx.x, gridDim.x);
+    const int cb = b % a.col_blocks;
+    const int lb = b / a.col_blocks;
+    const int l0 = lb * a.planes;
+    const int l1 = min(l0 + a.planes, a.nzv);
+    const double *__restrict__ dzv = HAS_Y ? g.dz : g.dy;
+    if ((int)threadIdx.x < l1 - l0) iz_s[threadIdx.x] = 1.0 / dzv[l0 + threadIdx.x];
+    __syncthreads();
+    const int ncols = a.nxv * a.nyv;
+    const int c = cb * 256 + threadIdx.x;
+    if (c >= ncols) return;
+    const int j = c % a.nxv;
+    const int k = c / a.nxv;
+    const double ix = 1.0 / g.dx[j];
+    const double iy = HAS_Y ? 1.0 / g.dy[k] : 0.0;
+    const int sx = (a.nxv + 1) * a.nyv;  // Fx plane size
+    const int sy = a.nxv * (a.nyv + 1);  // Fy plane size
+    const int sc = ncols;                // cell / marched-face plane size
+    const int n = sc * a.nzv;
+    const int ox = c + k;                // j + (nxv+1)*k
+    for (int v = 0; v < g.nvar; ++v) {
+        const double *__restrict__ FX = g.fx.p[v];
+        const double *__restrict__ FY = g.fy.p[v];
+        const double *__restrict__ FZ = HAS_Y ? g.fz.p[v] : g.fy.p[v];
+        double *__restrict__ R = g.rhs + v * n;
+        double zlo = FZ[c + sc * l0];
+#pragma unroll 4
+        for (int l = l0; l < l1; ++l) {
+            double r = face_term(FX[ox + sx * l], FX[ox + sx * l + 1], ix);
+            if (HAS_Y) r = add(r, face_term(FY[c + sy * l], FY[c + sy * l + a.nxv], iy));
+            const double zhi = FZ[c + sc * (l + 1)];
+            r = add(r, face_term(zlo, zhi, iz_s[l - l0]));
+            R[c + sc * l] = r;
+            zlo = zhi;
+        }
+    }
+}
+
+constexpr int kTargetWaves = 2048;
+
+}  // namespace
+
+int flux_launch(const PtrTable &fx, const PtrTable &fy, const PtrTable *fz, const double *dx,
+                const double *dy, const double *dz, int nvar, int nx, int ny, int nz, double *rhs, int map,
+                hipStream_t s) {
+    FluxArgs g{};
+    g.fx = fx;
+    g.fy = fy;
+    if (fz) g.fz = *fz;
+    g.dx = dx;
+    g.dy = dy;
+    g.dz = dz;
+    g.rhs = rhs;
+    g.nvar = nvar;
+    g.nx = nx;
+    g.ny = ny;
+    g.nz = nz;
+    const bool has_z = fz != nullptr;
+    const long n = (long)nx * ny * nz;
+    if (map == SGC_VAR_PER_CELL) {
+        const dim3 grid((unsigned)((n + 255) / 256));
+        if (has_z) hipLaunchKernelGGL((k_flux_per_cell<true>), grid, dim3(256), 0, s, g);
+        else hipLaunchKernelGGL((k_flux_per_cell<false>), grid, dim3(256), 0, s, g);
+        return check_launch("flux difference, one thread per cell");
+    }
+    if (map == SGC_VAR_PER_CELLVAR) {
+        const dim3 grid((unsigned)((n * nvar + 255) / 256));
+        if (has_z) hipLaunchKernelGGL((k_flux_per_cellvar<true>), grid, dim3(256), 0, s, g);
+        else hipLaunchKernelGGL((k_flux_per_cellvar<false>), grid, dim3(256), 0, s, g);
+        return check_launch("flux difference, one thread per (var, cell)");
+    }
+    if (map != SGC_VAR_TILED) return fail(SGC_EINVAL, "unknown variable map");
+    PencilArgs a;
+    a.g = g;
+    if (has_z) {
+        a.nxv = nx; a.nyv = ny; a.nzv = nz;
+    } else {
+        a.nxv = nx; a.nyv = 1; a.nzv = ny;
+    }
+    const long ncols = (long)a.nxv * a.nyv;
+    a.col_blocks = (int)((ncols + 255) / 256);
+    const long waves_per_run = (ncols + 63) / 64;
+    long runs = (kTargetWaves + waves_per_run - 1) / waves_per_run;
+    if (runs < 1) runs = 1;
+    int planes = (int)((a.nzv + runs - 1) / runs);
+    planes = planes < 4 ? 4 : planes;
+    planes = planes > kMaxPlanes ? kMaxPlanes : planes;
+    planes = planes > a.nzv ? a.nzv : planes;
+    a.planes = planes;
+    const long blocks = (long)a.col_blocks * ((a.nzv + planes - 1) / planes);
+    if (has_z) hipLaunchKernelGGL((k_flux_pencil<true>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_flux_pencil<false>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+    return check_launch("flux difference, column pencils");
+}
+
+}  // namespace sgc

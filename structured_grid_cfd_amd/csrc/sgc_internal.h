@@ -1,0 +1,53 @@
+// sgc_internal.h -- shared declarations of the HIP kernel launchers behind
+// the C ABI in include/sgc.h.  Internal to libsgc.so; gfx950 only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <string>
+
+#include "../../include/sgc.h"
+
+namespace sgc {
+
+// Records `msg` as the calling thread's last error and returns `code`.
+int fail(int code, const std::string &msg);
+
+// Launch-status check after an enqueue: SGC_EHIP with the runtime's message.
+int check_launch(const char *what);
+
+// Workgroups are dealt to the 8 XCDs of the chip round-robin (block b runs on
+// XCD b % 8).  This maps the hardware block index to a logical index such that
+// each XCD receives one contiguous range of logical blocks, so neighbouring
+// tiles, which share halo rows/columns and partial cache lines, meet in the
+// same 4 MB L2.  A bijection on [0, nb).
+__device__ __forceinline__ int xcd_remap(int b, int nb) {
+    const int q = nb >> 3, r = nb & 7;
+    const int x = b & 7, m = b >> 3;
+    return x * q + (x < r ? x : r) + m;
+}
+
+// ---- diffusion (diffuse2d.hip) --------------------------------------------
+struct DiffPlan {
+    int nx, ny, ld;
+    int time_block;  // TEMPORAL only
+    int tile_rows;   // 0 = automatic
+};
+int diffuse_zero_ring(void *buf, int dtype, int nx, int ny, int ld, hipStream_t s);
+int diffuse_sweep(const void *src, void *dst, int dtype, const DiffPlan &p,
+                  double alpha, int map, int steps_in_launch, hipStream_t s);
+
+// ---- per-variable field kernels (field_pack.hip, flux_diff.hip) ------------
+struct PtrTable {
+    const double *p[SGC_MAX_NVAR];
+};
+int pack_launch(const PtrTable &fields, int nvar, int nx, int ny, int nz, int dir,
+                double *out, int map, hipStream_t s);
+int unpack_launch(const double *packed, int nvar, int nx, int ny, int nz, int dir,
+                  const PtrTable &fields, int map, hipStream_t s);
+int flux_launch(const PtrTable &fx, const PtrTable &fy, const PtrTable *fz,
+                const double *dx, const double *dy, const double *dz, int nvar,
+                int nx, int ny, int nz, double *rhs, int map, hipStream_t s);
+
+}  // namespace sgc

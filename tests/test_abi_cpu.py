@@ -1,0 +1,144 @@
+"""The C-ABI library without a GPU: it loads, exports exactly what
+include/sgc.h declares, and its host-side logic (launch counting, argument
+validation before any enqueue) behaves as documented.  No call here reaches a
+kernel launch: every validation case fails before the library touches HIP."""
+import ctypes
+import subprocess
+
+import pytest
+
+from structured_grid_cfd_amd import binding as b
+
+EXPECTED = ["stencil_diffuse2d", "stencil_diffuse2d_launches", "field_pack", "field_unpack",
+            "flux_diff3d", "sgc_last_error", "sgc_abi_version"]
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not b.LIB_PATH.exists():
+        from structured_grid_cfd_amd import build
+        build.build()
+    return b.load()
+
+
+def test_header_declares_the_abi():
+    assert sorted(b.header_functions()) == sorted(EXPECTED)
+
+
+def test_exports_every_declared_symbol(lib):
+    for name in b.header_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", str(b.LIB_PATH)], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if ln.split() and ln.split()[-2] == "T"}
+    public = {s for s in exported if not s.startswith("_")}
+    assert public == set(EXPECTED)
+
+
+def test_abi_version(lib):
+    assert lib.sgc_abi_version() == 1
+    assert b.last_error() == ""
+
+
+@pytest.mark.parametrize("steps,tb,expect", [
+    (0, 4, 0), (1, 4, 1), (2, 4, 2), (4, 4, 2), (5, 4, 3), (8, 4, 2), (1000, 8, 126),
+    (1000, 12, 84), (32, 8, 4), (7, 12, 1), (8, 12, 2), (31, 12, 3), (32, 12, 4), (3, 2, 3)])
+def test_temporal_launch_count_parity(lib, steps, tb, expect):
+    """Launch count L = ceil(steps/T), plus one when its parity differs from
+    the step count's, so the alternating launches end in v iff steps is odd."""
+    L = b.stencil_diffuse2d_launches(steps, "temporal", tb)
+    assert L == expect
+    assert L % 2 == steps % 2
+    assert L <= steps or steps == 0
+    if steps:
+        assert -(-steps // L) <= tb
+
+
+def test_launch_count_other_maps(lib):
+    for m in ("collapse_branch", "contig", "strided", "tiled"):
+        assert b.stencil_diffuse2d_launches(17, m, 99) == 17
+    assert b.stencil_diffuse2d_launches(-1, "tiled", 1) == -1
+    assert b.stencil_diffuse2d_launches(5, "temporal", 0) == -1
+    assert b.stencil_diffuse2d_launches(5, "temporal", 13) == -1
+    assert b.stencil_diffuse2d_launches(5, 9, 1) == -1
+
+
+U, V = 0x10000, 0x90000  # fake, never dereferenced: every call below fails validation
+
+
+@pytest.mark.parametrize("args,code,msg", [
+    ((0, V, 1, 8, 8, 8, 0.1, 1, 3, 1, 0), 2, "non-NULL"),
+    ((U, V, 7, 8, 8, 8, 0.1, 1, 3, 1, 0), 3, "dtype"),
+    ((U, V, 1, 2, 8, 8, 0.1, 1, 3, 1, 0), 1, ">= 3"),
+    ((U, V, 1, 8, 2, 8, 0.1, 1, 3, 1, 0), 1, ">= 3"),
+    ((U, V, 1, 8, 8, 7, 0.1, 1, 3, 1, 0), 1, "ld"),
+    ((U, V, 1, 8, 8, 8, 0.1, -1, 3, 1, 0), 1, "steps"),
+    ((U, V, 1, 8, 8, 8, float("nan"), 1, 3, 1, 0), 1, "finite"),
+    ((U, V, 1, 8, 8, 8, float("inf"), 1, 3, 1, 0), 1, "finite"),
+    ((U, V, 1, 8, 8, 8, 0.1, 1, 5, 1, 0), 1, "map"),
+    ((U, V, 1, 8, 8, 8, 0.1, 1, 4, 0, 0), 1, "time_block"),
+    ((U, V, 1, 8, 8, 8, 0.1, 1, 4, 13, 0), 5, "time_block"),
+    ((U, V, 1, 8, 8, 8, 0.1, 1, 3, 1, 9), 1, "tile_rows"),
+    ((U, V, 1, 8, 8, 8, 0.1, 1, 3, 1, -1), 1, "tile_rows"),
+    ((U, V, 1, 70000, 70000, 70000, 0.1, 1, 3, 1, 0), 5, "2^31"),
+    ((U, U + 8 * 63, 1, 8, 8, 8, 0.1, 1, 3, 1, 0), 4, "overlap"),
+    ((U + 4, V, 1, 8, 8, 8, 0.1, 1, 3, 1, 0), 1, "aligned"),
+    ((U, V + 2, 0, 8, 8, 8, 0.1, 1, 3, 1, 0), 1, "aligned"),
+    ((U, U + 4 * 63, 0, 8, 8, 8, 0.1, 1, 3, 1, 0), 4, "overlap"),
+])
+def test_diffuse_validation(lib, args, code, msg):
+    rc = lib.stencil_diffuse2d(*args, None, None)
+    assert rc == code
+    assert msg in b.last_error()
+
+
+def _tab(*ptrs):
+    t = (ctypes.c_void_p * len(ptrs))()
+    for k, p in enumerate(ptrs):
+        t[k] = p
+    return t
+
+
+def test_pack_validation(lib):
+    f = _tab(U, U + 0x1000)
+    assert lib.field_pack(f, 0, 4, 4, 4, 0, V, 2, None) == 1
+    assert lib.field_pack(f, 33, 4, 4, 4, 0, V, 2, None) == 1
+    assert lib.field_pack(None, 2, 4, 4, 4, 0, V, 2, None) == 2
+    assert lib.field_pack(_tab(U, 0), 2, 4, 4, 4, 0, V, 2, None) == 2
+    assert "entry 1" in b.last_error()
+    assert lib.field_pack(f, 2, 4, 4, 4, 0, None, 2, None) == 2
+    assert lib.field_pack(f, 2, 4, 4, 4, 3, V, 2, None) == 1
+    assert lib.field_pack(f, 2, 4, 4, 4, 0, V, 3, None) == 1
+    assert lib.field_pack(f, 2, 0, 4, 4, 0, V, 2, None) == 1
+    assert lib.field_pack(f, 2, 2000, 2000, 1000, 0, V, 2, None) == 5
+    # out overlapping field 1
+    assert lib.field_pack(f, 2, 4, 4, 4, 0, U + 0x1000 + 8, 2, None) == 4
+    assert lib.field_unpack(V, 2, 4, 4, 4, 1, _tab(U, U + 8), 2, None) == 4
+    assert lib.field_unpack(U + 16, 2, 4, 4, 4, 1, _tab(U, U + 0x1000), 2, None) == 4
+    assert lib.field_unpack(None, 2, 4, 4, 4, 1, f, 2, None) == 2
+
+
+def test_flux_validation(lib):
+    fx, fy, fz = _tab(U), _tab(U + 0x1000), _tab(U + 0x2000)
+    d = U + 0x3000
+    assert lib.flux_diff3d(fx, fy, fz, d, d, d, 1, 4, 4, 4, V, 5, None) == 1
+    assert lib.flux_diff3d(None, fy, fz, d, d, d, 1, 4, 4, 4, V, 2, None) == 2
+    assert lib.flux_diff3d(fx, fy, fz, d, d, None, 1, 4, 4, 4, V, 2, None) == 2
+    assert lib.flux_diff3d(fx, fy, None, d, d, d, 1, 4, 4, 4, V, 2, None) == 2
+    assert lib.flux_diff3d(fx, fy, None, d, d, None, 1, 4, 4, 4, V, 2, None) == 1
+    assert "nz == 1" in b.last_error()
+    assert lib.flux_diff3d(fx, fy, fz, 0, d, d, 1, 4, 4, 4, V, 2, None) == 2
+    assert lib.flux_diff3d(fx, fy, fz, d, d, d, 1, 4, 4, 4, None, 2, None) == 2
+    assert lib.flux_diff3d(fx, fy, fz, d, d, d, 1, 4, 4, 4, U + 0x1000, 2, None) == 4
+    assert lib.flux_diff3d(fx, fy, fz, d, d, d, 1, 3000, 3000, 3000, V, 2, None) == 5
+    assert lib.flux_diff3d(fx, fy, fz, d, d, d, 1, 4, 4, 4, V + 4, 2, None) == 1
+    assert lib.flux_diff3d(_tab(U + 2), fy, fz, d, d, d, 1, 4, 4, 4, V, 2, None) == 1
+
+
+def test_last_error_is_per_call(lib):
+    lib.stencil_diffuse2d(0, 0, 1, 8, 8, 8, 0.1, 1, 3, 1, 0, None, None)
+    assert b.last_error() != ""
+    assert b.stencil_diffuse2d_launches(3, "tiled", 1) == 3
+    # a later failing call replaces the message
+    lib.field_pack(None, 1, 1, 1, 1, 0, V, 0, None)
+    assert "fields table" in b.last_error()

@@ -1,0 +1,152 @@
+"""Parity at the workloads' full sizes, in the launch configuration the
+benchmark times.
+
+* Diffusion, 4096^2 FP64/FP32 for 1000 steps and 16384^2 FP32 for 200 steps:
+  the oracle cannot run the whole grid in seconds, so sampled cells are
+  computed one by one on sub-grids that keep each cell's full domain of
+  dependence (``oracle.diffuse2d_window``); plus whole-grid comparisons at a
+  few steps, and the property that every mapping returns the same bits at the
+  full step count.
+* Pack (8 x 201^3 along x/y/z), flux difference (7 x 201x101x101), and the
+  2D workload (6 x 4800x1200 flux difference and x/y packs): whole outputs.
+"""
+import concurrent.futures as cf
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import assert_bitwise, dev, host, require_gpu, say
+from structured_grid_cfd_amd import binding, inputs, launch_config
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _gpu():
+    require_gpu()
+
+
+def _run(u0, v0, nx, alpha, steps, cfg):
+    u, v = dev(u0), dev(v0)
+    in_v = binding.stencil_diffuse2d(u, v, nx, alpha, steps, cfg["map"], cfg["time_block"],
+                                     cfg["tile_rows"])
+    torch.cuda.synchronize()
+    out = host(v if in_v else u)
+    del u, v
+    return out
+
+
+def _samples(nx, ny, steps, extra, seed):
+    """Corner, edge and interior cells (0-based (i, j))."""
+    pts = [(1, 1), (nx - 2, ny - 2), (1, ny // 2), (nx // 2, 1), (nx - 2, 1)]
+    g = np.random.Generator(np.random.PCG64(seed))
+    for _ in range(extra):
+        pts.append((int(g.integers(1, nx - 1)), int(g.integers(1, ny - 1))))
+    return pts
+
+
+def _check_samples(u0, got, nx, alpha, steps, pts):
+    with cf.ThreadPoolExecutor(max_workers=8) as ex:
+        futs = {ex.submit(oracle.diffuse2d_window, u0, nx, alpha, steps, i, j): (i, j) for i, j in pts}
+        for f in cf.as_completed(futs):
+            i, j = futs[f]
+            ref = f.result()
+            g = got[j, i]
+            assert np.asarray(g).view(np.uint64 if got.dtype == np.float64 else np.uint32) == \
+                np.asarray(ref).view(np.uint64 if got.dtype == np.float64 else np.uint32), \
+                (i, j, g, ref)
+
+
+@pytest.mark.parametrize("dt", ["f64", "f32"])
+def test_cfg2_4096_1000_steps_sampled(dt):
+    c = inputs.cfg2(np.float64 if dt == "f64" else np.float32)
+    cfg = launch_config.diffusion(dt)
+    say("cfg2 production", dt, cfg)
+    got = _run(c["u"], c["v"], c["nx"], c["alpha"], c["steps"], cfg)
+    assert np.all(np.isfinite(got)) and got.min() >= 0 and got.max() < 1
+    # an interior window of 2003^2 cells x 1000 steps is the costly one: one
+    _check_samples(c["u"], got, c["nx"], c["alpha"], c["steps"],
+                   _samples(c["nx"], c["ny"], c["steps"], 1, 2))
+
+
+@pytest.mark.parametrize("dt", ["f64", "f32"])
+def test_cfg2_4096_all_maps_whole_grid_few_steps(dt):
+    c = inputs.cfg2(np.float64 if dt == "f64" else np.float32, steps=6)
+    ref = oracle.diffuse2d_result(c["u"], c["nx"], 0.1, 6)
+    for m, tb in [("collapse_branch", 1), ("contig", 1), ("strided", 1), ("tiled", 1),
+                  ("temporal", 3), ("temporal", 6)]:
+        say("cfg2 6 steps", dt, m, tb)
+        got = _run(c["u"], c["v"], c["nx"], 0.1, 6, {"map": m, "time_block": tb, "tile_rows": 0})
+        assert_bitwise(got, ref, f"cfg2 {m} T={tb}")
+
+
+@pytest.mark.parametrize("dt", ["f64", "f32"])
+def test_cfg2_all_maps_agree_at_1000_steps(dt):
+    """The three page layouts and this library's sweeps return one bit
+    pattern after the full 1000 steps."""
+    c = inputs.cfg2(np.float64 if dt == "f64" else np.float32)
+    first = None
+    for m, tb in [("temporal", 8), ("tiled", 1), ("contig", 1), ("collapse_branch", 1),
+                  ("strided", 1), ("temporal", 12), ("temporal", 5)]:
+        say("cfg2 1000 steps", dt, m, tb)
+        got = _run(c["u"], c["v"], c["nx"], 0.1, c["steps"], {"map": m, "time_block": tb, "tile_rows": 0})
+        if first is None:
+            first = got
+        else:
+            assert_bitwise(got, first, f"{m} T={tb} vs temporal 8")
+
+
+def test_cfg5_16384_fp32_200_steps_sampled():
+    c = inputs.cfg5_diffusion()
+    cfg = launch_config.diffusion("f32")
+    say("cfg5 diffusion production", cfg)
+    got = _run(c["u"], c["v"], c["nx"], c["alpha"], c["steps"], cfg)
+    assert got.min() >= 0 and got.max() < 1
+    _check_samples(c["u"], got, c["nx"], c["alpha"], c["steps"],
+                   _samples(c["nx"], c["ny"], c["steps"], 24, 6))
+
+
+@pytest.mark.parametrize("direction", [0, 1, 2])
+def test_cfg3_pack_201cubed(direction):
+    f = inputs.cfg3()
+    ref = oracle.field_pack(f, direction)
+    fd = dev(f)
+    for m in ["tiled", "per_cell", "per_cellvar"]:
+        say("cfg3 pack", direction, m)
+        out = binding.field_pack(fd, direction, map=m)
+        torch.cuda.synchronize()
+        assert_bitwise(host(out), ref, f"cfg3 dir={direction} {m}")
+        del out
+
+
+def test_cfg4_flux_201x101x101():
+    fi = inputs.cfg4()
+    ref = oracle.flux_diff(fi.fx, fi.fy, fi.fz, fi.dx, fi.dy, fi.dz)
+    args = (dev(fi.fx), dev(fi.fy), dev(fi.fz), dev(fi.dx), dev(fi.dy), dev(fi.dz))
+    for m in ["tiled", "per_cell", "per_cellvar"]:
+        say("cfg4 flux", m)
+        rhs = binding.flux_diff3d(*args, map=m)
+        torch.cuda.synchronize()
+        assert_bitwise(host(rhs), ref, f"cfg4 {m}")
+
+
+def test_cfg5_2d_flux_and_packs():
+    fi = inputs.cfg5_flux()
+    ref = oracle.flux_diff(fi.fx, fi.fy, None, fi.dx, fi.dy, None)
+    args = (dev(fi.fx), dev(fi.fy), None, dev(fi.dx), dev(fi.dy), None)
+    for m in ["tiled", "per_cell", "per_cellvar"]:
+        say("cfg5 flux", m)
+        rhs = binding.flux_diff3d(*args, map=m)
+        torch.cuda.synchronize()
+        assert_bitwise(host(rhs), ref, f"cfg5 flux {m}")
+    f = inputs.cfg5_fields()
+    fd = dev(f)
+    for direction in (0, 1):
+        pref = oracle.field_pack(f, direction)
+        for m in ["tiled", "per_cell", "per_cellvar"]:
+            say("cfg5 pack", direction, m)
+            out = binding.field_pack(fd, direction, map=m)
+            torch.cuda.synchronize()
+            assert_bitwise(host(out), pref, f"cfg5 pack dir={direction} {m}")
