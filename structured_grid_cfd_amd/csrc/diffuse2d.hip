@@ -95,35 +95,86 @@ __global__ __launch_bounds__(256) void k_zero_ring(T *__restrict__ g, int nx, in
 // Marching strip sweep with optional temporal blocking
 // ---------------------------------------------------------------------------
 
-template <typename T> struct LaneVec;
-template <> struct LaneVec<float> {
-    static constexpr int K = 4;
+// One 16-byte vector: V elements.
+template <typename T> struct Vec16;
+template <> struct Vec16<float> {
+    static constexpr int V = 4;
     typedef float type __attribute__((ext_vector_type(4)));
 };
-template <> struct LaneVec<double> {
-    static constexpr int K = 2;
+template <> struct Vec16<double> {
+    static constexpr int V = 2;
     typedef double type __attribute__((ext_vector_type(2)));
 };
 
 // DPP wavefront shifts by one lane (GFX9 dpp_ctrl 0x138 wave_shr:1 and 0x130
-// wave_shl:1).  shr: lane l receives lane l-1's value; shl: lane l receives
-// lane l+1's.  Lanes without a source keep 0; they only ever feed the halo
-// columns that the march discards.
+// wave_shl:1) with bound_ctrl set: shr gives lane l the value of lane l-1,
+// shl the value of lane l+1, and the lane without a source receives 0.  Those
+// lanes only ever feed halo columns that the march discards.
 __device__ __forceinline__ float wave_shr1(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x138, 0xf, 0xf, false));
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x138, 0xf, 0xf, true));
 }
 __device__ __forceinline__ float wave_shl1(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x130, 0xf, 0xf, false));
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x130, 0xf, 0xf, true));
 }
 __device__ __forceinline__ double wave_shr1(double x) {
-    const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(x), 0x138, 0xf, 0xf, false);
-    const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(x), 0x138, 0xf, 0xf, false);
+    const int lo = __builtin_amdgcn_mov_dpp(__double2loint(x), 0x138, 0xf, 0xf, true);
+    const int hi = __builtin_amdgcn_mov_dpp(__double2hiint(x), 0x138, 0xf, 0xf, true);
     return __hiloint2double(hi, lo);
 }
 __device__ __forceinline__ double wave_shl1(double x) {
-    const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(x), 0x130, 0xf, 0xf, false);
-    const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(x), 0x130, 0xf, 0xf, false);
+    const int lo = __builtin_amdgcn_mov_dpp(__double2loint(x), 0x130, 0xf, 0xf, true);
+    const int hi = __builtin_amdgcn_mov_dpp(__double2hiint(x), 0x130, 0xf, 0xf, true);
     return __hiloint2double(hi, lo);
+}
+
+// Raw buffer descriptors (gfx9 layout: 48-bit base, stride 0, byte range,
+// config word 0x00020000).  Every access below is range-checked by the
+// hardware against the descriptor: a load outside [0, bytes) returns 0 and a
+// store outside it is dropped.  The march points each wave's load descriptor
+// at exactly the interior rows it may read and its store descriptor at exactly
+// the rows it owns, so boundary rows, halo rows and discarded lanes need no
+// branches around memory operations.
+constexpr uint32_t kOutOfRange = 0x80000000u;  // an offset no descriptor covers
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+// Loads 16 bytes into x[at .. at+V).
+template <int POL, typename T, int K>
+__device__ __forceinline__ void buf_load_vec(T (&x)[K], int at, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const i32x4 w = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, POL);
+    const typename Vec16<T>::type y = __builtin_bit_cast(typename Vec16<T>::type, w);
+#pragma unroll
+    for (int e = 0; e < Vec16<T>::V; ++e) x[at + e] = y[e];
+}
+template <int POL>
+__device__ __forceinline__ float buf_load_elem(float *, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, POL));
+}
+template <int POL>
+__device__ __forceinline__ double buf_load_elem(double *, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(double, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, POL));
+}
+// Stores x[at .. at+V) as 16 bytes.
+template <int POL, typename T, int K>
+__device__ __forceinline__ void buf_store_vec(const T (&x)[K], int at, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+    typename Vec16<T>::type y;
+#pragma unroll
+    for (int e = 0; e < Vec16<T>::V; ++e) y[e] = x[at + e];
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, y), r, off, 0, POL);
+}
+template <int POL>
+__device__ __forceinline__ void buf_store_elem(float x, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(x), r, off, 0, POL);
+}
+template <int POL>
+__device__ __forceinline__ void buf_store_elem(double x, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, x), r, off, 0, POL);
 }
 
 struct MarchArgs {
@@ -136,35 +187,64 @@ struct MarchArgs {
     double alpha;
 };
 
-template <typename T> constexpr int march_halo(int ts) {
-    return ((ts + LaneVec<T>::K - 1) / LaneVec<T>::K) * LaneVec<T>::K;
+// Strip geometry for KV 16-byte vectors per lane: K = KV*V columns per lane,
+// 64*K per wave; the halo is TS columns rounded up to whole vectors.
+template <typename T, int KV> constexpr int march_k() { return KV * Vec16<T>::V; }
+template <typename T, int KV> constexpr int march_halo(int ts) {
+    return ((ts + Vec16<T>::V - 1) / Vec16<T>::V) * Vec16<T>::V;
 }
-template <typename T> constexpr int march_out_width(int ts) {
-    return 64 * LaneVec<T>::K - 2 * march_halo<T>(ts);
+template <typename T, int KV> constexpr int march_out_width(int ts) {
+    return 64 * march_k<T, KV>() - 2 * march_halo<T, KV>(ts);
 }
 
-// One wave's march.  EDGE: the strip touches the first/last column or runs
-// past the grid, so per-element column masks are needed; interior strips
-// skip them.  VEC: 16-byte aligned rows, one vector load/store per lane-row.
-template <typename T, int TS, bool VEC, bool EDGE>
+// One wave's march over output rows [row_out0, row_out1) and output columns
+// [col_out0, col_out0 + OW).  EDGE: some computed cell can lie on or outside
+// the grid boundary (first/last strip, first/last row tiles), so per-cell
+// row/column masks force those cells to 0; interior tiles skip every mask.
+// VEC: 16-byte aligned rows, KV 16-byte accesses per lane and row.
+// LPOL/SPOL: cache policy bits of the loads/stores (2 = non-temporal).
+template <typename T, int TS, int KV, bool VEC, bool EDGE, int LPOL, int SPOL>
 __device__ __forceinline__ void march(const T *__restrict__ src, T *__restrict__ dst, int nx,
                                       int ny, int ld, T a, int lane, int col_out0,
                                       int row_out0, int row_out1) {
-    constexpr int K = LaneVec<T>::K;
-    constexpr int HALO = march_halo<T>(TS);
-    constexpr int OW = march_out_width<T>(TS);
-    typedef typename LaneVec<T>::type V;
+    constexpr int V = Vec16<T>::V;
+    constexpr int K = march_k<T, KV>();
+    constexpr int HALO = march_halo<T, KV>(TS);
+    constexpr int OW = march_out_width<T, KV>(TS);
+    constexpr int ES = (int)sizeof(T);
 
     const int c0 = col_out0 - HALO + lane * K;  // first column this lane holds
     bool colin[K];                              // column is an interior column
 #pragma unroll
     for (int e = 0; e < K; ++e) colin[e] = EDGE ? (c0 + e >= 1 && c0 + e <= nx - 2) : true;
-    const bool lane_out = c0 >= col_out0 && c0 < col_out0 + OW;
 
-    const int r_first = row_out0 - TS;        // first input row of the march
+    const int r_first = row_out0 - TS;       // first input row of the march
     const int nit = row_out1 - row_out0 + 2 * TS;
-    const int nit3 = ((nit + 2) / 3) * 3;     // three-phase unrolled loop
-    const int r_load_max = min(ny - 2, row_out1 - 1 + TS);
+    const int nit3 = ((nit + 2) / 3) * 3;    // three-phase unrolled loop
+
+    // Load descriptor: the interior rows this wave may read.
+    const int lr0 = max(1, r_first);
+    const int lr1 = min(ny - 2, row_out1 - 1 + TS);
+    const __amdgpu_buffer_rsrc_t rin =
+        make_rsrc(src + (long)lr0 * ld, lr1 >= lr0 ? (uint32_t)(lr1 - lr0 + 1) * (uint32_t)ld * ES : 0u);
+    // Store descriptor: the rows this wave owns.
+    const __amdgpu_buffer_rsrc_t rout =
+        make_rsrc(dst + (long)row_out0 * ld, (uint32_t)(row_out1 - row_out0) * (uint32_t)ld * ES);
+    const uint32_t row_bytes = (uint32_t)ld * ES;
+    // Byte offsets within a row.  Cells this lane must not store (halo
+    // columns, columns past nx) get an offset outside every descriptor.
+    uint32_t st_off[K];
+#pragma unroll
+    for (int e = 0; e < K; ++e) {
+        const int c = c0 + e;
+        st_off[e] = (c >= col_out0 && c < col_out0 + OW && (!EDGE || c < nx)) ? (uint32_t)c * ES : kOutOfRange;
+    }
+    uint32_t st_vec[KV];  // whole-vector stores (interior strips)
+#pragma unroll
+    for (int v = 0; v < KV; ++v) {
+        const int c = c0 + v * V;
+        st_vec[v] = (c >= col_out0 && c < col_out0 + OW) ? (uint32_t)c * ES : kOutOfRange;
+    }
 
     T win[TS][3][K];  // win[s][slot][e]: level-s rows, slot = row phase mod 3
     T pre[3][K];      // level-0 rows in flight, three rows ahead
@@ -175,35 +255,22 @@ __device__ __forceinline__ void march(const T *__restrict__ src, T *__restrict__
 #pragma unroll
             for (int e = 0; e < K; ++e) win[s][p][e] = T(0);
 
+    // Row r of the input: rows outside [lr0, lr1] read as 0 through the
+    // descriptor range (also rows 0 and ny-1, which are edge rows).
     auto load_row = [&](T (&x)[K], int r) {
-        if (r >= 1 && r <= r_load_max) {  // only interior rows are non-zero
-            const T *rowp = src + r * ld + c0;
-            if (VEC) {
-                V y = V(T(0));
-                if (!EDGE || (c0 >= 0 && c0 < nx)) y = *reinterpret_cast<const V *>(rowp);
+        const uint32_t roff = (uint32_t)(r - lr0) * row_bytes;
+        if (VEC) {
 #pragma unroll
-                for (int e = 0; e < K; ++e) x[e] = colin[e] ? y[e] : T(0);
-            } else {
-#pragma unroll
-                for (int e = 0; e < K; ++e) x[e] = colin[e] ? rowp[e] : T(0);
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < K; ++e) x[e] = T(0);
-        }
-    };
-
-    auto store_row = [&](const T (&x)[K], int q) {
-        T *rowp = dst + q * ld + c0;
-        if (VEC && (!EDGE || c0 + K <= nx)) {
-            V y;
-#pragma unroll
-            for (int e = 0; e < K; ++e) y[e] = x[e];
-            *reinterpret_cast<V *>(rowp) = y;
+            for (int v = 0; v < KV; ++v)
+                buf_load_vec<LPOL>(x, v * V, rin, roff + (uint32_t)(c0 + v * V) * ES);
         } else {
 #pragma unroll
             for (int e = 0; e < K; ++e)
-                if (!EDGE || c0 + e < nx) rowp[e] = x[e];
+                x[e] = buf_load_elem<LPOL>((T *)nullptr, rin, roff + (uint32_t)(c0 + e) * ES);
+        }
+        if (EDGE) {
+#pragma unroll
+            for (int e = 0; e < K; ++e) x[e] = colin[e] ? x[e] : T(0);
         }
     };
 
@@ -218,11 +285,14 @@ __device__ __forceinline__ void march(const T *__restrict__ src, T *__restrict__
 #pragma unroll
         for (int e = 0; e < K; ++e) win[0][P][e] = pre[P][e];
         load_row(pre[P], r + 3);
+        T out[K];
+#pragma unroll
+        for (int e = 0; e < K; ++e) out[e] = T(0);
 #pragma unroll
         for (int s = 1; s <= TS; ++s) {
             if (it >= 2 * s) {  // level s row r-s depends only on loaded rows
                 const int q = r - s;
-                const bool rowin = q >= 1 && q <= ny - 2;
+                const bool rowin = !EDGE || (q >= 1 && q <= ny - 2);
                 const T wl = wave_shr1(win[s - 1][PC][K - 1]);
                 const T er = wave_shl1(win[s - 1][PC][0]);
                 T res[K];
@@ -232,16 +302,27 @@ __device__ __forceinline__ void march(const T *__restrict__ src, T *__restrict__
                     const T ee = e == K - 1 ? er : win[s - 1][PC][e + 1];
                     T val = five_point(w, ee, win[s - 1][PS][e], win[s - 1][P][e],
                                        win[s - 1][PC][e], a);
-                    if (EDGE && !colin[e]) val = T(0);
-                    res[e] = rowin ? val : T(0);
+                    if (EDGE) val = (colin[e] && rowin) ? val : T(0);
+                    res[e] = val;
                 }
-                if (s < TS) {
 #pragma unroll
-                    for (int e = 0; e < K; ++e) win[s < TS ? s : 0][P][e] = res[e];
-                } else if (q >= row_out0 && q < row_out1 && lane_out) {
-                    store_row(res, q);
+                for (int e = 0; e < K; ++e) {
+                    if (s < TS)
+                        win[s < TS ? s : 0][P][e] = res[e];
+                    else
+                        out[e] = res[e];
                 }
             }
+        }
+        // Row r-TS of the last level; rows outside [row_out0, row_out1) and
+        // discarded cells fall outside the store descriptor and are dropped.
+        const uint32_t qoff = (uint32_t)(r - TS - row_out0) * row_bytes;
+        if (VEC && !EDGE) {
+#pragma unroll
+            for (int v = 0; v < KV; ++v) buf_store_vec<SPOL>(out, v * V, rout, qoff + st_vec[v]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < K; ++e) buf_store_elem<SPOL>(out[e], rout, qoff + st_off[e]);
         }
     };
 
@@ -252,14 +333,17 @@ __device__ __forceinline__ void march(const T *__restrict__ src, T *__restrict__
     }
 }
 
-template <typename T, int TS, bool VEC>
+template <typename T, int TS, int KV, bool VEC, int LPOL, int SPOL>
 __global__ __launch_bounds__(256) void k_march(MarchArgs g) {
-    constexpr int K = LaneVec<T>::K;
-    constexpr int HALO = march_halo<T>(TS);
-    constexpr int OW = march_out_width<T>(TS);
+    constexpr int K = march_k<T, KV>();
+    constexpr int HALO = march_halo<T, KV>(TS);
+    constexpr int OW = march_out_width<T, KV>(TS);
     static_assert(OW > 0, "time block too deep for the strip width");
     const int lane = threadIdx.x & 63;
-    const int tile = xcd_remap(blockIdx.x, gridDim.x) * 4 + (threadIdx.x >> 6);
+    // The wave index is uniform across the wave; saying so keeps the tile
+    // coordinates, and the buffer descriptors built from them, in SGPRs.
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int tile = xcd_remap(blockIdx.x, gridDim.x) * 4 + wave;
     if (tile >= g.ntiles) return;  // whole wave leaves; the kernel has no barriers
     const int strip = tile % g.nstrips;
     const int rtile = tile / g.nstrips;
@@ -270,27 +354,35 @@ __global__ __launch_bounds__(256) void k_march(MarchArgs g) {
     T *dst = static_cast<T *>(g.dst);
     const T a = T(g.alpha);
     const int span0 = col_out0 - HALO;  // first column of the strip
-    const bool interior = span0 >= 1 && span0 + 64 * K <= g.nx - 1;
+    // Computed rows run from row_out0 - TS + 1 to row_out1 + TS + 1 (the
+    // three-phase loop may run two rows past the last needed one).
+    const bool interior = span0 >= 1 && span0 + 64 * K <= g.nx - 1 && row_out0 - TS >= 0 &&
+                          row_out1 + TS + 2 <= g.ny - 2;
     if (interior)
-        march<T, TS, VEC, false>(src, dst, g.nx, g.ny, g.ld, a, lane, col_out0, row_out0, row_out1);
+        march<T, TS, KV, VEC, false, LPOL, SPOL>(src, dst, g.nx, g.ny, g.ld, a, lane, col_out0,
+                                                 row_out0, row_out1);
     else
-        march<T, TS, VEC, true>(src, dst, g.nx, g.ny, g.ld, a, lane, col_out0, row_out0, row_out1);
+        march<T, TS, KV, VEC, true, LPOL, SPOL>(src, dst, g.nx, g.ny, g.ld, a, lane, col_out0,
+                                                row_out0, row_out1);
 }
 
 // ---------------------------------------------------------------------------
 // Host-side launch selection
 // ---------------------------------------------------------------------------
 
-constexpr int kTargetTiles = 4096;  // ~16 waves per CU over 256 CUs
+// Launch shape (chosen from sweeps on MI355X): vectors per lane, cache
+// policies, and the tile height as a function of the fused depth.
+constexpr int kLoadPolicy = 0;   // cache policy bits of the march's loads
+constexpr int kStorePolicy = 0;  // ... and of its stores
+// One 16-byte vector per lane: two (wider strips, half the halo) cost more
+// registers than they save and measured slower at every depth.
+template <typename T> constexpr int vectors_per_lane(int) { return 1; }
+// Tiles of TS > 1: about 8192 waves over the grid, rows between 4*TS (the
+// halo rows are 2*TS per tile) and 128.
+constexpr long kTargetTiles = 8192;
 
-template <typename T> int out_width(int ts) {
-    const int K = LaneVec<T>::K;
-    const int halo = ((ts + K - 1) / K) * K;
-    return 64 * K - 2 * halo;
-}
-
-template <typename T, int TS>
-int launch_march_ts(const void *src, void *dst, const DiffPlan &p, double alpha, hipStream_t s) {
+template <typename T, int TS, int KV>
+int launch_march_kv(const void *src, void *dst, const DiffPlan &p, double alpha, hipStream_t s) {
     MarchArgs g;
     g.src = src;
     g.dst = dst;
@@ -298,27 +390,44 @@ int launch_march_ts(const void *src, void *dst, const DiffPlan &p, double alpha,
     g.ny = p.ny;
     g.ld = p.ld;
     g.alpha = alpha;
-    const int ow = out_width<T>(TS);
+    const int ow = march_out_width<T, KV>(TS);
     g.nstrips = (p.nx + ow - 1) / ow;
     int rows = p.tile_rows;
     if (rows <= 0) {
-        const int chunks = (kTargetTiles + g.nstrips - 1) / g.nstrips;
-        rows = (p.ny + chunks - 1) / chunks;
-        rows = max(rows, max(16, 4 * TS));
+        if (TS == 1) {
+            rows = 8;  // short tiles: many waves in flight beat long marches
+        } else {
+            rows = (int)((long)p.ny * g.nstrips / kTargetTiles);
+            rows = max(4 * TS, min(rows, 128));
+        }
     }
     rows = min(rows, p.ny);
+    // Keep every descriptor within 2^30 bytes and every offset a wave can
+    // form (its rows plus the halo and prefetch rows around them) below
+    // 2^30, so that offsets outside a wave's rows, and the out-of-range
+    // marker added to any of them, never land back inside a descriptor.
+    const long row_bytes = (long)p.ld * (long)sizeof(T);
+    const long max_rows = (1L << 30) / row_bytes - 2 * TS - 8;
+    if (max_rows < 1) return fail(SGC_ERANGE, "grid rows too wide for the marching sweep");
+    rows = (int)min((long)rows, max_rows);
     g.tile_rows = rows;
     const long ntiles = (long)g.nstrips * ((p.ny + rows - 1) / rows);
+    if (ntiles > 0x7fffffffL - 3) return fail(SGC_ERANGE, "too many tiles");
     g.ntiles = (int)ntiles;
     const int blocks = (int)((ntiles + 3) / 4);
     const bool vec = (reinterpret_cast<uintptr_t>(src) % 16 == 0) &&
                      (reinterpret_cast<uintptr_t>(dst) % 16 == 0) &&
                      ((long)p.ld * (long)sizeof(T)) % 16 == 0;
     if (vec)
-        hipLaunchKernelGGL((k_march<T, TS, true>), dim3(blocks), dim3(256), 0, s, g);
+        hipLaunchKernelGGL((k_march<T, TS, KV, true, kLoadPolicy, kStorePolicy>), dim3(blocks), dim3(256), 0, s, g);
     else
-        hipLaunchKernelGGL((k_march<T, TS, false>), dim3(blocks), dim3(256), 0, s, g);
+        hipLaunchKernelGGL((k_march<T, TS, KV, false, kLoadPolicy, kStorePolicy>), dim3(blocks), dim3(256), 0, s, g);
     return check_launch("diffusion march kernel");
+}
+
+template <typename T, int TS>
+int launch_march_ts(const void *src, void *dst, const DiffPlan &p, double alpha, hipStream_t s) {
+    return launch_march_kv<T, TS, vectors_per_lane<T>(TS)>(src, dst, p, alpha, s);
 }
 
 template <typename T>
