@@ -7,9 +7,9 @@
 //   * k_collapse_branch, k_contig, k_strided -- the three loop layouts of
 //     section 5.1-5.3 (flattened grid with an edge branch; workgroup per row
 //     with lanes along i; workgroup per column with lanes along j);
-//   * k_march<T, TS, VEC> -- this library's sweep: one wave owns a strip of
-//     64*K columns (K elements per lane = one 16-byte load) and marches up a
-//     tile of rows, keeping a three-row register window per time level.
+//   * k_march<T, TS, KV, ...> -- this library's sweep: one wave owns a strip
+//     of 64*K columns (K elements per lane = one 16-byte load) and marches up
+//     a tile of rows, keeping a three-row register window per time level.
 //     West/east neighbours cross lanes with DPP wave shifts, north/south come
 //     from the window, so every input row is read from memory exactly once and
 //     every output row written once per launch.  TS > 1 fuses TS time steps in
@@ -17,7 +17,10 @@
 //     each side and the tile TS extra rows above and below, recomputed
 //     redundantly, which section 5.4 notes is what a correct fusion across
 //     steps needs.  Every cell of a level is produced by the same expression as
-//     a single step, so all mappings give identical bits.
+//     a single step, so all mappings give identical bits.  Memory goes through
+//     raw buffer instructions whose range check supplies the zero rows and
+//     drops stores outside the wave's rows, so the loop has no branches around
+//     memory and its prefetch waits stay partial.
 #include "sgc_internal.h"
 
 namespace sgc {
