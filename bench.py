@@ -212,10 +212,12 @@ def measure_all(log) -> dict:
     from structured_grid_cfd_amd import binding, inputs, launch_config
 
     stream = torch.cuda.current_stream()
-    flush_buf = torch.empty(256 * 1024 * 1024, dtype=torch.float32, device="cuda")  # 1 GiB
+    flush_buf = torch.ones(256 * 1024 * 1024, dtype=torch.float32, device="cuda")  # 1 GiB
 
     def flush():
-        flush_buf.zero_()  # evicts the 256 MB MALL and the L2s
+        # Reading 1 GiB evicts the 256 MB MALL and the L2s; a write would leave
+        # dirty lines whose write-back then overlaps the timed kernel.
+        flush_buf.sum()
 
     def timed(fn, reps, do_flush):
         out = []

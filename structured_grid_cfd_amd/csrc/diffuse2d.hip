@@ -130,20 +130,10 @@ __device__ __forceinline__ double wave_shl1(double x) {
     return __hiloint2double(hi, lo);
 }
 
-// Raw buffer descriptors (gfx9 layout: 48-bit base, stride 0, byte range,
-// config word 0x00020000).  Every access below is range-checked by the
-// hardware against the descriptor: a load outside [0, bytes) returns 0 and a
-// store outside it is dropped.  The march points each wave's load descriptor
-// at exactly the interior rows it may read and its store descriptor at exactly
-// the rows it owns, so boundary rows, halo rows and discarded lanes need no
-// branches around memory operations.
-constexpr uint32_t kOutOfRange = 0x80000000u;  // an offset no descriptor covers
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
-                                             0x00020000);
-}
-
+// Memory goes through raw buffer descriptors (sgc_internal.h): the march
+// points each wave's load descriptor at exactly the interior rows it may read
+// and its store descriptor at exactly the rows it owns, so boundary rows, halo
+// rows and discarded lanes need no branches around memory operations.
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 

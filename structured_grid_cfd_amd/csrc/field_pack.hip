@@ -11,9 +11,10 @@
 //     does (the page's "before");
 //   * PER_CELL -- one thread per cell, index math once, variables looped
 //     inside the thread (the page's "after");
-//   * TILED -- x: 16-byte streaming copies per variable (the x pack is a
-//     concatenation); y/z: 64x64 tiles transposed through LDS so that both the
-//     read and the write side move whole 512-byte row segments.
+//   * TILED -- x: 16-byte streaming copies per variable (the x
+//     pack is a concatenation); y/z: balanced tiles of at most 64x64
+//     transposed through LDS so that both the read and the write side move
+//     contiguous row segments.
 #include "sgc_internal.h"
 
 namespace sgc {
@@ -73,53 +74,90 @@ __global__ __launch_bounds__(256) void k_pack_per_cellvar(PackArgs g) {
         g.out[o] = g.f.p[v][c];
 }
 
-// x direction, TILED: per variable a straight copy of n doubles.  Each block
-// copies `chunk` elements; when source and destination share their 16-byte
-// phase, one peeled element aligns both and the body moves 16-byte vectors,
-// four in flight per thread.
+// x direction (and the identity cases), TILED: per variable a straight copy
+// of n doubles.  Each workgroup moves one chunk of kChunkVec 16-byte vectors
+// (four per thread, all loads issued before the stores).  Loads are
+// non-temporal (nothing re-reads the source), which measured 10-15% faster
+// than plain loads; stores stay ordinary (non-temporal stores were slower).  When source and
+// destination share their 16-byte phase, element 0 is peeled (if needed) so
+// both are aligned; otherwise the chunk falls back to 8-byte copies.
+constexpr int kChunkVec = 4 * 256;
+
 template <bool UNPACK>
-__global__ __launch_bounds__(256) void k_copy_x(PackArgs g, int chunk) {
+__global__ __launch_bounds__(256) void k_copy(PackArgs g, int chunks_per_var) {
     typedef double d2 __attribute__((ext_vector_type(2)));
-    const int v = blockIdx.y;
+    const int b = xcd_remap(blockIdx.x, gridDim.x);
+    const int v = b / chunks_per_var;
+    const int chunk = b - v * chunks_per_var;
     const int n = g.nx * g.ny * g.nz;
     const double *__restrict__ src = UNPACK ? g.packed + (long)v * n : g.f.p[v];
     double *__restrict__ dst = UNPACK ? const_cast<double *>(g.f.p[v]) : g.out + (long)v * n;
-    const int b0 = blockIdx.x * chunk;
-    if (b0 >= n) return;
-    const int b1 = min(b0 + chunk, n);
     const int tid = threadIdx.x;
-    const uintptr_t sa = reinterpret_cast<uintptr_t>(src + b0), da = reinterpret_cast<uintptr_t>(dst + b0);
-    if (((sa ^ da) & 15) != 0) {  // phases differ: 8-byte copies
-        for (int i = b0 + tid; i < b1; i += 256) dst[i] = src[i];
+    const uintptr_t sa = reinterpret_cast<uintptr_t>(src), da = reinterpret_cast<uintptr_t>(dst);
+    if (((sa ^ da) & 15) != 0) {  // phases differ: 8-byte copies, two vectors' worth each
+        const int e0 = chunk * 2 * kChunkVec;
+        double t[8];
+        if (e0 + 2 * kChunkVec <= n) {  // whole chunk in range
+#pragma unroll
+            for (int u = 0; u < 8; ++u) t[u] = __builtin_nontemporal_load(src + e0 + u * 256 + tid);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) *(dst + e0 + u * 256 + tid) = t[u];
+            return;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int i = e0 + u * 256 + tid;
+            t[u] = i < n ? __builtin_nontemporal_load(src + i) : 0.0;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int i = e0 + u * 256 + tid;
+            if (i < n) *(dst + i) = t[u];
+        }
         return;
     }
-    int h = b0 + ((sa & 15) ? 1 : 0);
-    if (h > b1) h = b1;
-    if (tid < h - b0) dst[b0 + tid] = src[b0 + tid];
-    const int nvec = (b1 - h) >> 1;
+    const int h = (sa & 15) ? 1 : 0;  // peeled head element
+    const int nvec = (n - h) >> 1;
+    if (chunk == 0 && tid == 0) {
+        if (h) dst[0] = src[0];
+        if ((n - h) & 1) dst[n - 1] = src[n - 1];
+    }
     const d2 *__restrict__ s2 = reinterpret_cast<const d2 *>(src + h);
     d2 *__restrict__ t2 = reinterpret_cast<d2 *>(dst + h);
-    int i = tid;
-    for (; i + 3 * 256 < nvec; i += 4 * 256) {
-        const d2 a0 = s2[i], a1 = s2[i + 256], a2 = s2[i + 512], a3 = s2[i + 768];
-        t2[i] = a0;
-        t2[i + 256] = a1;
-        t2[i + 512] = a2;
-        t2[i + 768] = a3;
+    const int i0 = chunk * kChunkVec + tid;
+    d2 t[4];
+    if ((chunk + 1) * kChunkVec <= nvec) {  // whole chunk in range: no per-element tests
+#pragma unroll
+        for (int u = 0; u < 4; ++u) t[u] = __builtin_nontemporal_load(s2 + i0 + u * 256);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) *(t2 + i0 + u * 256) = t[u];
+        return;
     }
-    for (; i < nvec; i += 256) t2[i] = s2[i];
-    if (((b1 - h) & 1) && tid == 0) dst[b1 - 1] = src[b1 - 1];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u * 256;
+        t[u] = i < nvec ? __builtin_nontemporal_load(s2 + i) : d2(0.0);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u * 256;
+        if (i < nvec) *(t2 + i) = t[u];
+    }
 }
 
 // Generic batched transpose through LDS.  in(x, y) = in_base[x + y*s_in]
-// (x contiguous), out(x, y) = out_base[y + x*s_out] (y contiguous).  One
-// 64x64 tile per workgroup of four waves: each wave reads 16 row segments of
-// 64 contiguous x, then writes 16 segments of 64 contiguous y.
+// (x contiguous), out(x, y) = out_base[y + x*s_out] (y contiguous).  Tiles of
+// TX x TY (each at most 64) split X and Y into equal parts, so no tile is a
+// thin remainder that costs a full tile's time for a few elements (201 =
+// 4 x 51 rather than 3 x 64 + 9).  One tile per workgroup of four waves: the
+// waves read rows of TX contiguous x, then write rows of TY contiguous y.
 struct TransArgs {
     PtrTable f;
     const double *packed;
     double *out;
     int X, Y;          // extents of the contiguous input / output indices
+    int TX, TY;        // tile extents (<= 64)
+    int ntx, nty;      // tiles along X and Y
     int s_in, s_out;   // strides of the other index on each side
     int P;             // planes per variable
     int p_in, p_out;   // plane offsets on each side
@@ -130,33 +168,46 @@ struct TransArgs {
 template <bool UNPACK>
 __global__ __launch_bounds__(256) void k_transpose(TransArgs g) {
     __shared__ double tile[64][65];
-    const int ntx = (g.X + 63) >> 6, nty = (g.Y + 63) >> 6;
     int t = xcd_remap(blockIdx.x, gridDim.x);
-    const int tx = t % ntx;
-    t /= ntx;
-    const int ty = t % nty;
-    t /= nty;
+    const int tx = t % g.ntx;
+    t /= g.ntx;
+    const int ty = t % g.nty;
+    t /= g.nty;
     const int p = t % g.P;
     const int v = t / g.P;
-    const double *__restrict__ in =
-        UNPACK ? g.packed + v * g.v_in + p * g.p_in : g.f.p[v] + p * g.p_in;
-    double *__restrict__ out =
-        UNPACK ? const_cast<double *>(g.f.p[v]) + p * g.p_out : g.out + v * g.v_out + p * g.p_out;
-    const int x0 = tx << 6, y0 = ty << 6;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const bool xin = x0 + lane < g.X;
+    const int x0 = tx * g.TX, y0 = ty * g.TY;
+    const int w = min(g.TX, g.X - x0), h = min(g.TY, g.Y - y0);
+    const double *in = (UNPACK ? g.packed + v * g.v_in : g.f.p[v]) + p * g.p_in + x0 + y0 * g.s_in;
+    double *out = (UNPACK ? const_cast<double *>(g.f.p[v]) : g.out + v * g.v_out) + p * g.p_out +
+                  y0 + x0 * g.s_out;
+    // Descriptors span exactly this tile's rows; elements outside the tile
+    // get an out-of-range offset, so every load and store below is issued
+    // unconditionally (all sixteen loads are in flight before the first use).
+    const __amdgpu_buffer_rsrc_t rin = make_rsrc(in, (uint32_t)(w + (h - 1) * g.s_in) * 8u);
+    const __amdgpu_buffer_rsrc_t rout = make_rsrc(out, (uint32_t)(h + (w - 1) * g.s_out) * 8u);
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    double val[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        const int yy = w + 4 * i;
-        if (xin && y0 + yy < g.Y) tile[yy][lane] = in[(x0 + lane) + (y0 + yy) * g.s_in];
+        const int yy = wv + 4 * i;
+        const uint32_t off = (lane < w && yy < h) ? (uint32_t)(lane + yy * g.s_in) * 8u : kOutOfRange;
+        val[i] = buf_load_f64<2>(rin, off);  // each element is read once: non-temporal
     }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) tile[wv + 4 * i][lane] = val[i];
     __syncthreads();
-    const bool yin = y0 + lane < g.Y;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        const int xx = w + 4 * i;
-        if (yin && x0 + xx < g.X) out[(y0 + lane) + (x0 + xx) * g.s_out] = tile[lane][xx];
+        const int xx = wv + 4 * i;
+        const uint32_t off = (lane < h && xx < w) ? (uint32_t)(lane + xx * g.s_out) * 8u : kOutOfRange;
+        buf_store_f64(tile[lane][xx], rout, off);
     }
+}
+
+// Equal split of n into ceil(n / 64) parts of at most 64.
+inline int balanced_tile(int n) {
+    const int parts = (n + 63) / 64;
+    return (n + parts - 1) / parts;
 }
 
 // How the TILED map moves one variable.  With every extent > 1, y pairs j
@@ -201,7 +252,14 @@ int launch_transpose(const PackArgs &a, Layout lay, hipStream_t s) {
         g.X = fY; g.Y = fX; g.s_in = pS; g.s_out = fS;
         g.P = P; g.p_in = pP; g.p_out = fP; g.v_in = n; g.v_out = 0;
     }
-    const long tiles = (long)((g.X + 63) / 64) * ((g.Y + 63) / 64) * g.P * g.nvar;
+    // Buffer offsets inside one tile must stay below 2^31.
+    if ((long)64 * (g.s_in + 1) * 8 >= (1L << 31) || (long)64 * (g.s_out + 1) * 8 >= (1L << 31))
+        return -1;
+    g.TX = balanced_tile(g.X);
+    g.TY = balanced_tile(g.Y);
+    g.ntx = (g.X + g.TX - 1) / g.TX;
+    g.nty = (g.Y + g.TY - 1) / g.TY;
+    const long tiles = (long)g.ntx * g.nty * g.P * g.nvar;
     if (tiles > 0x7fffffffL) return fail(SGC_ERANGE, "transpose grid too large");
     hipLaunchKernelGGL((k_transpose<UNPACK>), dim3((unsigned)tiles), dim3(256), 0, s, g);
     return check_launch("pack transpose");
@@ -227,12 +285,16 @@ int launch_pack(const PackArgs &g, int dir, int map, hipStream_t s) {
     if (map == SGC_VAR_TILED) {
         const Layout lay = tiled_layout(dir, g.nx, g.ny, g.nz);
         if (lay == Layout::Copy) {
-            const int chunk = 8192;
-            const dim3 grid((n + chunk - 1) / chunk, g.nvar);
-            hipLaunchKernelGGL((k_copy_x<UNPACK>), grid, dim3(256), 0, s, g, chunk);
+            const long per_var = ((long)n + 2L * kChunkVec - 1) / (2L * kChunkVec);
+            const long blocks = per_var * g.nvar;
+            if (blocks > 0x7fffffffL) return fail(SGC_ERANGE, "copy grid too large");
+            hipLaunchKernelGGL((k_copy<UNPACK>), dim3((unsigned)blocks), dim3(256), 0, s, g, (int)per_var);
             return check_launch("pack, streaming copy");
         }
-        return launch_transpose<UNPACK>(g, lay, s);
+        const int rc = launch_transpose<UNPACK>(g, lay, s);
+        if (rc != -1) return rc;
+        // Strides too large for 32-bit tile offsets: one thread per cell.
+        return launch_pack<UNPACK>(g, dir, SGC_VAR_PER_CELL, s);
     }
     return fail(SGC_EINVAL, "unknown variable map");
 }

@@ -15,8 +15,10 @@
 //   * TILED -- one thread per (j, k) column marching a run of l planes: the
 //     high z face of plane l is kept in a register as the low face of plane
 //     l+1, so every face is read from memory once; 1/dx and 1/dy are formed
-//     once per column and 1/dz once per plane per workgroup (in LDS).  The 2D
-//     form marches along k instead, treating Fy as the marched face.
+//     once per column and 1/dz once per plane per workgroup (in LDS); the
+//     variables advance in groups of four so each plane step has twenty
+//     independent loads in flight.  The 2D form marches along k instead,
+//     treating Fy as the marched face.
 #include "sgc_internal.h"
 
 namespace sgc {
@@ -102,6 +104,11 @@ struct PencilArgs {
     int col_blocks;   // workgroups across the nxv*nyv columns
 };
 
+// Variables are marched in groups of VG: per plane step a thread issues the
+// 5*VG face loads of the group at once, which is what keeps enough bytes in
+// flight with only a few thousand waves.
+constexpr int kVarGroup = 4;
+
 template <bool HAS_Y>
 __global__ __launch_bounds__(256) void k_flux_pencil(PencilArgs a) {
     __shared__ double iz_s[kMaxPlanes];
@@ -126,25 +133,54 @@ __global__ __launch_bounds__(256) void k_flux_pencil(PencilArgs a) {
     const int sc = ncols;                // cell / marched-face plane size
     const int n = sc * a.nzv;
     const int ox = c + k;                // j + (nxv+1)*k
-    for (int v = 0; v < g.nvar; ++v) {
-        const double *__restrict__ FX = g.fx.p[v];
-        const double *__restrict__ FY = g.fy.p[v];
-        const double *__restrict__ FZ = HAS_Y ? g.fz.p[v] : g.fy.p[v];
-        double *__restrict__ R = g.rhs + v * n;
-        double zlo = FZ[c + sc * l0];
-#pragma unroll 4
+    constexpr int VG = kVarGroup;
+    for (int v0 = 0; v0 < g.nvar; v0 += VG) {
+        // Members past the last variable repeat it: they load the same faces
+        // and store the same bits to the same cells from the same thread, which
+        // keeps the loop free of branches around its loads.
+        const double *__restrict__ FX[VG];
+        const double *__restrict__ FY[VG];
+        const double *__restrict__ FZ[VG];
+        double *__restrict__ R[VG];
+#pragma unroll
+        for (int u = 0; u < VG; ++u) {
+            const int v = min(v0 + u, g.nvar - 1);
+            FX[u] = g.fx.p[v];
+            FY[u] = g.fy.p[v];
+            FZ[u] = HAS_Y ? g.fz.p[v] : g.fy.p[v];
+            R[u] = g.rhs + (long)v * n;
+        }
+        double zlo[VG];
+#pragma unroll
+        for (int u = 0; u < VG; ++u) zlo[u] = FZ[u][c + sc * l0];
         for (int l = l0; l < l1; ++l) {
-            double r = face_term(FX[ox + sx * l], FX[ox + sx * l + 1], ix);
-            if (HAS_Y) r = add(r, face_term(FY[c + sy * l], FY[c + sy * l + a.nxv], iy));
-            const double zhi = FZ[c + sc * (l + 1)];
-            r = add(r, face_term(zlo, zhi, iz_s[l - l0]));
-            R[c + sc * l] = r;
-            zlo = zhi;
+            double xl[VG], xh[VG], yl[VG], yh[VG], zh[VG];
+#pragma unroll
+            for (int u = 0; u < VG; ++u) {
+                xl[u] = FX[u][ox + sx * l];
+                xh[u] = FX[u][ox + sx * l + 1];
+                if (HAS_Y) {
+                    yl[u] = FY[u][c + sy * l];
+                    yh[u] = FY[u][c + sy * l + a.nxv];
+                }
+                zh[u] = FZ[u][c + sc * (l + 1)];
+            }
+            const double iz = iz_s[l - l0];
+#pragma unroll
+            for (int u = 0; u < VG; ++u) {
+                double r = face_term(xl[u], xh[u], ix);
+                if (HAS_Y) r = add(r, face_term(yl[u], yh[u], iy));
+                r = add(r, face_term(zlo[u], zh[u], iz));
+                R[u][c + sc * l] = r;
+                zlo[u] = zh[u];
+            }
         }
     }
 }
 
-constexpr int kTargetWaves = 2048;
+// Waves over the grid: the plane run per thread is chosen so the launch has
+// about this many (16k measured best: more waves, more loads in flight).
+constexpr int kTargetWaves = 16384;
 
 }  // namespace
 
@@ -191,7 +227,7 @@ int flux_launch(const PtrTable &fx, const PtrTable &fy, const PtrTable *fz, cons
     long runs = (kTargetWaves + waves_per_run - 1) / waves_per_run;
     if (runs < 1) runs = 1;
     int planes = (int)((a.nzv + runs - 1) / runs);
-    planes = planes < 4 ? 4 : planes;
+    planes = planes < 2 ? 2 : planes;
     planes = planes > kMaxPlanes ? kMaxPlanes : planes;
     planes = planes > a.nzv ? a.nzv : planes;
     a.planes = planes;

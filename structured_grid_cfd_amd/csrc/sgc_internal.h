@@ -28,6 +28,29 @@ __device__ __forceinline__ int xcd_remap(int b, int nb) {
     return x * q + (x < r ? x : r) + m;
 }
 
+// Raw buffer descriptors (gfx9 layout: 48-bit base, stride 0, byte range,
+// config word 0x00020000).  Accesses are range-checked by the hardware
+// against the descriptor: a load outside [0, bytes) returns 0 and a store
+// outside it is dropped.  Kernels use this to mask elements without branching
+// around memory instructions (branches there make the compiler wait for every
+// outstanding load before continuing, serialising the memory pipeline).
+constexpr uint32_t kOutOfRange = 0x80000000u;  // an offset no descriptor covers
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+// POL: cache policy bits (2 = non-temporal: the line is not expected to be
+// re-read, which streams it past the caches).
+template <int POL = 0>
+__device__ __forceinline__ double buf_load_f64(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(double, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, POL));
+}
+__device__ __forceinline__ void buf_store_f64(double x, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+    typedef int i32x2 __attribute__((ext_vector_type(2)));
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, x), r, off, 0, 0);
+}
+
 // ---- diffusion (diffuse2d.hip) --------------------------------------------
 struct DiffPlan {
     int nx, ny, ld;
