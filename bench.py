@@ -64,6 +64,9 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-steps", type=int, default=400,
                    help="sweeps of the CPU-baseline sample (same grid)")
+    p.add_argument("--ref-copy", action="store_true",
+                   help="first run one 1 GiB copy (1 GiB read + 1 GiB written) as a known-size "
+                        "reference for profiler byte counters")
     return p.parse_args()
 
 
@@ -99,6 +102,14 @@ def main():
         cfg["map"] = "temporal" if args.time_block > 1 else cfg["map"]
     if args.tile_rows is not None:
         cfg["tile_rows"] = args.tile_rows
+
+    if args.ref_copy:
+        n = 128 * 1024 * 1024
+        src = torch.ones((1, 1, 1, n), dtype=torch.float64, device="cuda")
+        dst = torch.empty_like(src)
+        binding.field_pack(src, 0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     # ---------------- headline: 4096^2, 1000 sweeps per step -----------------
     c = inputs.cfg2(dtype)

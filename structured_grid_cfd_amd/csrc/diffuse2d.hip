@@ -196,7 +196,7 @@ template <typename T, int KV> constexpr int march_out_width(int ts) {
 // row/column masks force those cells to 0; interior tiles skip every mask.
 // VEC: 16-byte aligned rows, KV 16-byte accesses per lane and row.
 // LPOL/SPOL: cache policy bits of the loads/stores (2 = non-temporal).
-template <typename T, int TS, int KV, bool VEC, bool EDGE, int LPOL, int SPOL>
+template <typename T, int TS, int KV, bool VEC, bool EDGE, bool DOWN, int LPOL, int SPOL>
 __device__ __forceinline__ void march(const T *__restrict__ src, T *__restrict__ dst, int nx,
                                       int ny, int ld, T a, int lane, int col_out0,
                                       int row_out0, int row_out1) {
@@ -211,12 +211,17 @@ __device__ __forceinline__ void march(const T *__restrict__ src, T *__restrict__
 #pragma unroll
     for (int e = 0; e < K; ++e) colin[e] = EDGE ? (c0 + e >= 1 && c0 + e <= nx - 2) : true;
 
-    const int r_first = row_out0 - TS;       // first input row of the march
+    // DOWN marches from the top of the tile to its bottom (rows decreasing);
+    // vertically adjacent tiles march in opposite directions so that the halo
+    // rows they share are read by both at about the same time, while they are
+    // still in L2.
+    constexpr int DR = DOWN ? -1 : 1;        // row step of the march
+    const int r_first = DOWN ? row_out1 - 1 + TS : row_out0 - TS;  // first input row
     const int nit = row_out1 - row_out0 + 2 * TS;
     const int nit3 = ((nit + 2) / 3) * 3;    // three-phase unrolled loop
 
     // Load descriptor: the interior rows this wave may read.
-    const int lr0 = max(1, r_first);
+    const int lr0 = max(1, row_out0 - TS);
     const int lr1 = min(ny - 2, row_out1 - 1 + TS);
     const __amdgpu_buffer_rsrc_t rin =
         make_rsrc(src + (long)lr0 * ld, lr1 >= lr0 ? (uint32_t)(lr1 - lr0 + 1) * (uint32_t)ld * ES : 0u);
@@ -268,23 +273,27 @@ __device__ __forceinline__ void march(const T *__restrict__ src, T *__restrict__
     };
 
 #pragma unroll
-    for (int p = 0; p < 3; ++p) load_row(pre[p], r_first + p);
+    for (int p = 0; p < 3; ++p) load_row(pre[p], r_first + DR * p);
 
     auto step = [&](auto phase, int it) {
         constexpr int P = decltype(phase)::value;
         constexpr int PC = (P + 2) % 3;  // previous row (centre for the next level)
-        constexpr int PS = (P + 1) % 3;  // row before that (south)
-        const int r = r_first + it;
+        constexpr int PO = (P + 1) % 3;  // row before that
+        // Rows q-1 (south) and q+1 (north) of the level below: marching up the
+        // newest row is north, marching down it is south.
+        constexpr int PSOUTH = DOWN ? P : PO;
+        constexpr int PNORTH = DOWN ? PO : P;
+        const int r = r_first + DR * it;
 #pragma unroll
         for (int e = 0; e < K; ++e) win[0][P][e] = pre[P][e];
-        load_row(pre[P], r + 3);
+        load_row(pre[P], r + DR * 3);
         T out[K];
 #pragma unroll
         for (int e = 0; e < K; ++e) out[e] = T(0);
 #pragma unroll
         for (int s = 1; s <= TS; ++s) {
-            if (it >= 2 * s) {  // level s row r-s depends only on loaded rows
-                const int q = r - s;
+            if (it >= 2 * s) {  // level s row r - DR*s depends only on loaded rows
+                const int q = r - DR * s;
                 const bool rowin = !EDGE || (q >= 1 && q <= ny - 2);
                 const T wl = wave_shr1(win[s - 1][PC][K - 1]);
                 const T er = wave_shl1(win[s - 1][PC][0]);
@@ -293,7 +302,7 @@ __device__ __forceinline__ void march(const T *__restrict__ src, T *__restrict__
                 for (int e = 0; e < K; ++e) {
                     const T w = e == 0 ? wl : win[s - 1][PC][e - 1];
                     const T ee = e == K - 1 ? er : win[s - 1][PC][e + 1];
-                    T val = five_point(w, ee, win[s - 1][PS][e], win[s - 1][P][e],
+                    T val = five_point(w, ee, win[s - 1][PSOUTH][e], win[s - 1][PNORTH][e],
                                        win[s - 1][PC][e], a);
                     if (EDGE) val = (colin[e] && rowin) ? val : T(0);
                     res[e] = val;
@@ -307,9 +316,9 @@ __device__ __forceinline__ void march(const T *__restrict__ src, T *__restrict__
                 }
             }
         }
-        // Row r-TS of the last level; rows outside [row_out0, row_out1) and
-        // discarded cells fall outside the store descriptor and are dropped.
-        const uint32_t qoff = (uint32_t)(r - TS - row_out0) * row_bytes;
+        // Row r - DR*TS of the last level; rows outside [row_out0, row_out1)
+        // and discarded cells fall outside the store descriptor and are dropped.
+        const uint32_t qoff = (uint32_t)(r - DR * TS - row_out0) * row_bytes;
         if (VEC && !EDGE) {
 #pragma unroll
             for (int v = 0; v < KV; ++v) buf_store_vec<SPOL>(out, v * V, rout, qoff + st_vec[v]);
@@ -347,16 +356,25 @@ __global__ __launch_bounds__(256) void k_march(MarchArgs g) {
     T *dst = static_cast<T *>(g.dst);
     const T a = T(g.alpha);
     const int span0 = col_out0 - HALO;  // first column of the strip
-    // Computed rows run from row_out0 - TS + 1 to row_out1 + TS + 1 (the
-    // three-phase loop may run two rows past the last needed one).
-    const bool interior = span0 >= 1 && span0 + 64 * K <= g.nx - 1 && row_out0 - TS >= 0 &&
+    // Rows formed at any level lie within [row_out0 - TS - 2, row_out1 + TS + 1]
+    // (the three-phase loop may run two rows past the last needed one).
+    const bool interior = span0 >= 1 && span0 + 64 * K <= g.nx - 1 && row_out0 - TS - 2 >= 1 &&
                           row_out1 + TS + 2 <= g.ny - 2;
-    if (interior)
-        march<T, TS, KV, VEC, false, LPOL, SPOL>(src, dst, g.nx, g.ny, g.ld, a, lane, col_out0,
-                                                 row_out0, row_out1);
-    else
-        march<T, TS, KV, VEC, true, LPOL, SPOL>(src, dst, g.nx, g.ny, g.ld, a, lane, col_out0,
-                                                row_out0, row_out1);
+    if (rtile & 1) {
+        if (interior)
+            march<T, TS, KV, VEC, false, true, LPOL, SPOL>(src, dst, g.nx, g.ny, g.ld, a, lane,
+                                                           col_out0, row_out0, row_out1);
+        else
+            march<T, TS, KV, VEC, true, true, LPOL, SPOL>(src, dst, g.nx, g.ny, g.ld, a, lane,
+                                                          col_out0, row_out0, row_out1);
+    } else {
+        if (interior)
+            march<T, TS, KV, VEC, false, false, LPOL, SPOL>(src, dst, g.nx, g.ny, g.ld, a, lane,
+                                                            col_out0, row_out0, row_out1);
+        else
+            march<T, TS, KV, VEC, true, false, LPOL, SPOL>(src, dst, g.nx, g.ny, g.ld, a, lane,
+                                                           col_out0, row_out0, row_out1);
+    }
 }
 
 // ---------------------------------------------------------------------------
