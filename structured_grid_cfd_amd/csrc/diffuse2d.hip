@@ -21,6 +21,8 @@
 //     raw buffer instructions whose range check supplies the zero rows and
 //     drops stores outside the wave's rows, so the loop has no branches around
 //     memory and its prefetch waits stay partial.
+#include <atomic>
+
 #include "sgc_internal.h"
 
 namespace sgc {
@@ -335,8 +337,16 @@ __device__ __forceinline__ void march(const T *__restrict__ src, T *__restrict__
     }
 }
 
+// Minimum waves per SIMD requested from the register allocator: FP64 at
+// depth 7-8 needs 129-130 VGPRs unconstrained; capping it at 128 admits a
+// fourth wave per SIMD without spilling, which gives the tile-height choice
+// below 4096 resident waves to fill instead of 3072.
+template <typename T> constexpr int march_min_waves(int ts) {
+    return (sizeof(T) == 8 && (ts == 7 || ts == 8)) ? 4 : 1;
+}
+
 template <typename T, int TS, int KV, bool VEC, int LPOL, int SPOL>
-__global__ __launch_bounds__(256) void k_march(MarchArgs g) {
+__global__ __launch_bounds__(256, march_min_waves<T>(TS)) void k_march(MarchArgs g) {
     constexpr int K = march_k<T, KV>();
     constexpr int HALO = march_halo<T, KV>(TS);
     constexpr int OW = march_out_width<T, KV>(TS);
@@ -382,15 +392,88 @@ __global__ __launch_bounds__(256) void k_march(MarchArgs g) {
 // ---------------------------------------------------------------------------
 
 // Launch shape (chosen from sweeps on MI355X): vectors per lane, cache
-// policies, and the tile height as a function of the fused depth.
+// policies, and the tile height.
 constexpr int kLoadPolicy = 0;   // cache policy bits of the march's loads
 constexpr int kStorePolicy = 0;  // ... and of its stores
 // One 16-byte vector per lane: two (wider strips, half the halo) cost more
 // registers than they save and measured slower at every depth.
 template <typename T> constexpr int vectors_per_lane(int) { return 1; }
-// Tiles of TS > 1: about 8192 waves over the grid, rows between 4*TS (the
-// halo rows are 2*TS per tile) and 128.
-constexpr long kTargetTiles = 8192;
+
+// Tile height for fused depths of five or more.  Such a launch is bound by
+// vector-ALU issue, and a SIMD holding w resident waves takes about
+// w x (rows + 2*TS + 3) row steps divided by the efficiency of w resident
+// waves.  Tile counts just above a multiple of the SIMD count put one more
+// wave on some SIMDs, or start a short extra round, and sweeps show those
+// 10-30% slower; so each candidate takes the lowest height whose tile count
+// fits w waves per SIMD exactly, for w = 1..occupancy (one round) and for
+// whole rounds of `occupancy` waves, and the cheapest candidate wins.  Tiles
+// taller than 128 rows measured 3-7% slower on grids too large to stay in
+// the on-package cache, so taller candidates are left out.  Efficiency of a
+// SIMD running w march waves, relative to four, from sweeps over
+// 2048^2..16384^2 grids at depths 6-10 in FP64 and FP32 on MI355X:
+constexpr double kWaveEfficiency[] = {0.0, 0.55, 0.85, 0.95, 1.0};
+constexpr long kMaxTileRows = 128;
+
+long march_tile_rows(long ny, long nstrips, int ts, int occupancy, long simds, long max_rows) {
+    const long cap = max_rows < kMaxTileRows ? max_rows : kMaxTileRows;
+    double best = 0.0;
+    long best_rows = -1;
+    auto consider = [&](long waves_per_simd, double eff) {
+        const long row_tiles = waves_per_simd * simds / nstrips;
+        if (row_tiles < 1) return;
+        const long rows = (ny + row_tiles - 1) / row_tiles;
+        if (rows > cap) return;
+        const double cost = (double)waves_per_simd * (double)(rows + 2 * ts + 3) / eff;
+        if (best_rows < 0 || cost < best) {
+            best = cost;
+            best_rows = rows;
+        }
+    };
+    for (int w = 1; w <= occupancy; ++w) consider(w, kWaveEfficiency[w < 4 ? w : 4]);
+    // Whole rounds: the fewest that bring the height under the cap (more
+    // rounds only add halo rows).
+    const long slots = (long)occupancy * simds;
+    const long row_tiles_needed = (ny + cap - 1) / cap;
+    long rounds = (row_tiles_needed * nstrips + slots - 1) / slots;
+    if (rounds < 2) rounds = 2;
+    consider(rounds * occupancy, kWaveEfficiency[occupancy < 4 ? occupancy : 4]);
+    return best_rows > 0 ? best_rows : cap;
+}
+
+// Resident workgroups of `kernel` per CU and the device's CU count, queried
+// once per device and cached.  A 256-thread workgroup puts one wave on each
+// SIMD of a CU, so workgroups per CU is also waves per SIMD.
+constexpr int kMaxDevices = 64;
+struct SlotCache {
+    std::atomic<int> per_cu[kMaxDevices];
+    std::atomic<int> cus[kMaxDevices];
+};
+int resident_slots(const void *kernel, SlotCache &cache, int *per_cu, int *cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(SGC_EHIP, "hipGetDevice failed");
+    if (dev >= 0 && dev < kMaxDevices) {
+        const int p = cache.per_cu[dev].load(std::memory_order_relaxed);
+        const int c = cache.cus[dev].load(std::memory_order_relaxed);
+        if (p > 0 && c > 0) {
+            *per_cu = p;
+            *cus = c;
+            return SGC_OK;
+        }
+    }
+    int p = 0, c = 0;
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&p, kernel, 256, 0);
+    if (e != hipSuccess) return fail(SGC_EHIP, std::string("occupancy query: ") + hipGetErrorString(e));
+    e = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return fail(SGC_EHIP, std::string("CU count query: ") + hipGetErrorString(e));
+    if (p < 1 || c < 1) return fail(SGC_EHIP, "the march kernel cannot be resident on this device");
+    if (dev >= 0 && dev < kMaxDevices) {
+        cache.per_cu[dev].store(p, std::memory_order_relaxed);
+        cache.cus[dev].store(c, std::memory_order_relaxed);
+    }
+    *per_cu = p;
+    *cus = c;
+    return SGC_OK;
+}
 
 template <typename T, int TS, int KV>
 int launch_march_kv(const void *src, void *dst, const DiffPlan &p, double alpha, hipStream_t s) {
@@ -403,16 +486,6 @@ int launch_march_kv(const void *src, void *dst, const DiffPlan &p, double alpha,
     g.alpha = alpha;
     const int ow = march_out_width<T, KV>(TS);
     g.nstrips = (p.nx + ow - 1) / ow;
-    int rows = p.tile_rows;
-    if (rows <= 0) {
-        if (TS == 1) {
-            rows = 8;  // short tiles: many waves in flight beat long marches
-        } else {
-            rows = (int)((long)p.ny * g.nstrips / kTargetTiles);
-            rows = max(4 * TS, min(rows, 128));
-        }
-    }
-    rows = min(rows, p.ny);
     // Keep every descriptor within 2^30 bytes and every offset a wave can
     // form (its rows plus the halo and prefetch rows around them) below
     // 2^30, so that offsets outside a wave's rows, and the out-of-range
@@ -420,19 +493,34 @@ int launch_march_kv(const void *src, void *dst, const DiffPlan &p, double alpha,
     const long row_bytes = (long)p.ld * (long)sizeof(T);
     const long max_rows = (1L << 30) / row_bytes - 2 * TS - 8;
     if (max_rows < 1) return fail(SGC_ERANGE, "grid rows too wide for the marching sweep");
-    rows = (int)min((long)rows, max_rows);
-    g.tile_rows = rows;
+    const bool vec = (reinterpret_cast<uintptr_t>(src) % 16 == 0) &&
+                     (reinterpret_cast<uintptr_t>(dst) % 16 == 0) &&
+                     ((long)p.ld * (long)sizeof(T)) % 16 == 0;
+    auto kernel = vec ? k_march<T, TS, KV, true, kLoadPolicy, kStorePolicy>
+                      : k_march<T, TS, KV, false, kLoadPolicy, kStorePolicy>;
+    long rows = p.tile_rows;
+    if (rows <= 0) {
+        if (TS <= 3) {
+            rows = 8;  // memory bound: many short tiles in flight
+        } else if (TS == 4) {
+            // Between memory and ALU bound: about 8192 tiles of 16 to 128 rows.
+            rows = max(16L, min((long)p.ny * g.nstrips / 8192, 128L));
+        } else {
+            static SlotCache cache[2];
+            int per_cu = 0, cus = 0;
+            const int rc = resident_slots(reinterpret_cast<const void *>(kernel), cache[vec], &per_cu, &cus);
+            if (rc != SGC_OK) return rc;
+            rows = march_tile_rows(p.ny, g.nstrips, TS, per_cu, 4L * cus, max_rows);
+        }
+    }
+    rows = min(rows, (long)p.ny);
+    rows = min(rows, max_rows);
+    g.tile_rows = (int)rows;
     const long ntiles = (long)g.nstrips * ((p.ny + rows - 1) / rows);
     if (ntiles > 0x7fffffffL - 3) return fail(SGC_ERANGE, "too many tiles");
     g.ntiles = (int)ntiles;
     const int blocks = (int)((ntiles + 3) / 4);
-    const bool vec = (reinterpret_cast<uintptr_t>(src) % 16 == 0) &&
-                     (reinterpret_cast<uintptr_t>(dst) % 16 == 0) &&
-                     ((long)p.ld * (long)sizeof(T)) % 16 == 0;
-    if (vec)
-        hipLaunchKernelGGL((k_march<T, TS, KV, true, kLoadPolicy, kStorePolicy>), dim3(blocks), dim3(256), 0, s, g);
-    else
-        hipLaunchKernelGGL((k_march<T, TS, KV, false, kLoadPolicy, kStorePolicy>), dim3(blocks), dim3(256), 0, s, g);
+    hipLaunchKernelGGL(kernel, dim3(blocks), dim3(256), 0, s, g);
     return check_launch("diffusion march kernel");
 }
 
