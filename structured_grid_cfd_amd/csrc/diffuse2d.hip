@@ -40,6 +40,23 @@ __device__ __forceinline__ T five_point(T w, T e, T s, T n, T c, T a) {
     return c + a * t;
 }
 
+// The same bits through one fused multiply-add.  Scaling by 4 is exact
+// whenever the product is finite, so fma(-4, c, t) rounds t - 4c once exactly
+// as the separate subtraction does (signed zeros and subnormals included);
+// valid only while |4c| stays below the overflow threshold, which the march
+// checks on every tile it computes this way.
+__device__ __forceinline__ float fma_op(float x, float y, float z) { return __builtin_fmaf(x, y, z); }
+__device__ __forceinline__ double fma_op(double x, double y, double z) { return __builtin_fma(x, y, z); }
+template <typename T>
+__device__ __forceinline__ T five_point_fused(T w, T e, T s, T n, T c, T a) {
+#pragma clang fp contract(off)
+    T t = w + e;
+    t = t + s;
+    t = t + n;
+    t = fma_op(T(-4), c, t);
+    return c + a * t;
+}
+
 // ---------------------------------------------------------------------------
 // The pages' three loop layouts
 // ---------------------------------------------------------------------------
@@ -180,6 +197,7 @@ struct MarchArgs {
     int ntiles;     // nstrips * row tiles
     int tile_rows;  // output rows per tile
     double alpha;
+    double fuse_limit;  // fused form allowed while sum |input| stays below this
 };
 
 // Strip geometry for KV 16-byte vectors per lane: K = KV*V columns per lane,
@@ -198,9 +216,13 @@ template <typename T, int KV> constexpr int march_out_width(int ts) {
 // row/column masks force those cells to 0; interior tiles skip every mask.
 // VEC: 16-byte aligned rows, KV 16-byte accesses per lane and row.
 // LPOL/SPOL: cache policy bits of the loads/stores (2 = non-temporal).
-template <typename T, int TS, int KV, bool VEC, bool EDGE, bool DOWN, int LPOL, int SPOL>
-__device__ __forceinline__ void march(const T *__restrict__ src, T *__restrict__ dst, int nx,
-                                      int ny, int ld, T a, int lane, int col_out0,
+// FUSED: cells use five_point_fused, and the lane adds up |x| over every value
+// it loads; the return value is true when that sum is not below `limit` (or is
+// NaN), in which case the stored results may differ from the separate form
+// and the caller recomputes the tile with FUSED off.
+template <typename T, int TS, int KV, bool VEC, bool EDGE, bool DOWN, int LPOL, int SPOL, bool FUSED>
+__device__ __forceinline__ bool march(const T *__restrict__ src, T *__restrict__ dst, int nx,
+                                      int ny, int ld, T a, T limit, int lane, int col_out0,
                                       int row_out0, int row_out1) {
     constexpr int V = Vec16<T>::V;
     constexpr int K = march_k<T, KV>();
@@ -255,6 +277,8 @@ __device__ __forceinline__ void march(const T *__restrict__ src, T *__restrict__
 #pragma unroll
             for (int e = 0; e < K; ++e) win[s][p][e] = T(0);
 
+    T checksum = T(0);  // FUSED: sum of |x| over the lane's loads
+
     // Row r of the input: rows outside [lr0, lr1] read as 0 through the
     // descriptor range (also rows 0 and ny-1, which are edge rows).
     auto load_row = [&](T (&x)[K], int r) {
@@ -271,6 +295,10 @@ __device__ __forceinline__ void march(const T *__restrict__ src, T *__restrict__
         if (EDGE) {
 #pragma unroll
             for (int e = 0; e < K; ++e) x[e] = colin[e] ? x[e] : T(0);
+        }
+        if (FUSED) {
+#pragma unroll
+            for (int e = 0; e < K; ++e) checksum = checksum + __builtin_fabs(x[e]);
         }
     };
 
@@ -304,8 +332,10 @@ __device__ __forceinline__ void march(const T *__restrict__ src, T *__restrict__
                 for (int e = 0; e < K; ++e) {
                     const T w = e == 0 ? wl : win[s - 1][PC][e - 1];
                     const T ee = e == K - 1 ? er : win[s - 1][PC][e + 1];
-                    T val = five_point(w, ee, win[s - 1][PSOUTH][e], win[s - 1][PNORTH][e],
-                                       win[s - 1][PC][e], a);
+                    T val = FUSED ? five_point_fused(w, ee, win[s - 1][PSOUTH][e], win[s - 1][PNORTH][e],
+                                                     win[s - 1][PC][e], a)
+                                  : five_point(w, ee, win[s - 1][PSOUTH][e], win[s - 1][PNORTH][e],
+                                               win[s - 1][PC][e], a);
                     if (EDGE) val = (colin[e] && rowin) ? val : T(0);
                     res[e] = val;
                 }
@@ -335,18 +365,11 @@ __device__ __forceinline__ void march(const T *__restrict__ src, T *__restrict__
         step(std::integral_constant<int, 1>{}, it + 1);
         step(std::integral_constant<int, 2>{}, it + 2);
     }
-}
-
-// Minimum waves per SIMD requested from the register allocator: FP64 at
-// depth 7-8 needs 129-130 VGPRs unconstrained; capping it at 128 admits a
-// fourth wave per SIMD without spilling, which gives the tile-height choice
-// below 4096 resident waves to fill instead of 3072.
-template <typename T> constexpr int march_min_waves(int ts) {
-    return (sizeof(T) == 8 && (ts == 7 || ts == 8)) ? 4 : 1;
+    return FUSED && !(checksum < limit);
 }
 
 template <typename T, int TS, int KV, bool VEC, int LPOL, int SPOL>
-__global__ __launch_bounds__(256, march_min_waves<T>(TS)) void k_march(MarchArgs g) {
+__global__ __launch_bounds__(256) void k_march(MarchArgs g) {
     constexpr int K = march_k<T, KV>();
     constexpr int HALO = march_halo<T, KV>(TS);
     constexpr int OW = march_out_width<T, KV>(TS);
@@ -370,20 +393,33 @@ __global__ __launch_bounds__(256, march_min_waves<T>(TS)) void k_march(MarchArgs
     // (the three-phase loop may run two rows past the last needed one).
     const bool interior = span0 >= 1 && span0 + 64 * K <= g.nx - 1 && row_out0 - TS - 2 >= 1 &&
                           row_out1 + TS + 2 <= g.ny - 2;
+    const T limit = T(g.fuse_limit);
+    // Interior tiles take the fused form; a wave whose inputs could push 4c
+    // past the overflow threshold recomputes its tile in the separate form
+    // (same stores, now with the definition's bits).  Edge tiles always use
+    // the separate form.
     if (rtile & 1) {
-        if (interior)
-            march<T, TS, KV, VEC, false, true, LPOL, SPOL>(src, dst, g.nx, g.ny, g.ld, a, lane,
-                                                           col_out0, row_out0, row_out1);
-        else
-            march<T, TS, KV, VEC, true, true, LPOL, SPOL>(src, dst, g.nx, g.ny, g.ld, a, lane,
-                                                          col_out0, row_out0, row_out1);
+        if (interior) {
+            const bool redo = march<T, TS, KV, VEC, false, true, LPOL, SPOL, true>(
+                src, dst, g.nx, g.ny, g.ld, a, limit, lane, col_out0, row_out0, row_out1);
+            if (__any(redo))
+                march<T, TS, KV, VEC, true, true, LPOL, SPOL, false>(
+                    src, dst, g.nx, g.ny, g.ld, a, limit, lane, col_out0, row_out0, row_out1);
+        } else {
+            march<T, TS, KV, VEC, true, true, LPOL, SPOL, false>(src, dst, g.nx, g.ny, g.ld, a, limit,
+                                                                 lane, col_out0, row_out0, row_out1);
+        }
     } else {
-        if (interior)
-            march<T, TS, KV, VEC, false, false, LPOL, SPOL>(src, dst, g.nx, g.ny, g.ld, a, lane,
-                                                            col_out0, row_out0, row_out1);
-        else
-            march<T, TS, KV, VEC, true, false, LPOL, SPOL>(src, dst, g.nx, g.ny, g.ld, a, lane,
-                                                           col_out0, row_out0, row_out1);
+        if (interior) {
+            const bool redo = march<T, TS, KV, VEC, false, false, LPOL, SPOL, true>(
+                src, dst, g.nx, g.ny, g.ld, a, limit, lane, col_out0, row_out0, row_out1);
+            if (__any(redo))
+                march<T, TS, KV, VEC, true, false, LPOL, SPOL, false>(
+                    src, dst, g.nx, g.ny, g.ld, a, limit, lane, col_out0, row_out0, row_out1);
+        } else {
+            march<T, TS, KV, VEC, true, false, LPOL, SPOL, false>(src, dst, g.nx, g.ny, g.ld, a, limit,
+                                                                  lane, col_out0, row_out0, row_out1);
+        }
     }
 }
 
@@ -475,6 +511,19 @@ int resident_slots(const void *kernel, SlotCache &cache, int *per_cu, int *cus) 
     return SGC_OK;
 }
 
+// Largest sum of |input| over a wave's loads for which no level of a TS-deep
+// fused launch can bring 4c near overflow.  One level grows the largest
+// magnitude by at most 1 + 8|alpha| exactly, times the rounding of its six
+// operations (1 + 2^-16 covers FP32 and FP64); inputs below the limit keep
+// |c| <= 2^(emax-2) (2^1021, 2^125) at every level, so 4c and the partial
+// sums stay finite.  A NaN or infinite alpha gives 0: never fused.
+template <typename T> double march_fuse_limit(double alpha, int ts) {
+    const double growth = (1.0 + 8.0 * __builtin_fabs(alpha)) * (1.0 + 0x1p-16);
+    double lim = sizeof(T) == 8 ? 0x1p1021 : 0x1p125;
+    for (int i = 0; i < ts; ++i) lim /= growth;
+    return lim > 0.0 ? lim : 0.0;
+}
+
 template <typename T, int TS, int KV>
 int launch_march_kv(const void *src, void *dst, const DiffPlan &p, double alpha, hipStream_t s) {
     MarchArgs g;
@@ -484,6 +533,7 @@ int launch_march_kv(const void *src, void *dst, const DiffPlan &p, double alpha,
     g.ny = p.ny;
     g.ld = p.ld;
     g.alpha = alpha;
+    g.fuse_limit = march_fuse_limit<T>(alpha, TS);
     const int ow = march_out_width<T, KV>(TS);
     g.nstrips = (p.nx + ow - 1) / ow;
     // Keep every descriptor within 2^30 bytes and every offset a wave can

@@ -57,3 +57,16 @@ def oracle_diffuse(u0, v0, nx, alpha, steps):
     u, v = u0.copy(), v0.copy()
     in_v = oracle.diffuse2d(u, v, nx, alpha, steps)
     return (v if in_v else u), in_v
+
+
+def assert_bitwise_nan(got: np.ndarray, ref: np.ndarray, what: str = ""):
+    """Bitwise equality where every NaN counts as equal to every NaN: the sign
+    and payload of a NaN made by inf - inf are the platform's choice, not the
+    definition's (x86 and gfx950 differ), so only NaN positions are compared."""
+    gn, rn = np.isnan(got), np.isnan(ref)
+    if not np.array_equal(gn, rn):
+        bad = np.argwhere(gn != rn)
+        first = tuple(bad[0])
+        raise AssertionError(f"{what}: NaN positions differ at {len(bad)} elements; first at "
+                             f"{first}: got {got[first]!r} expected {ref[first]!r}")
+    assert_bitwise(np.where(gn, 0, got).astype(got.dtype), np.where(rn, 0, ref).astype(ref.dtype), what)

@@ -1,0 +1,83 @@
+"""GPU parity of the marching sweep's interior tiles, which compute
+t - 4c through one fused multiply-add (the same rounding while 4c is finite)
+and fall back to the separate form when a tile's inputs are large enough for
+4c to overflow, or hold NaN or infinity.
+
+Grids are large enough for many tiles away from every edge; magnitudes cover
+the ordinary range, values near the largest the fused form accepts, the
+subnormal range, and cells that force the fallback.  Every result is compared
+with the oracle bit for bit (NaN positions only, where inf - inf occurs).
+"""
+import numpy as np
+import pytest
+
+from gpu_helpers import (assert_bitwise, assert_bitwise_nan, gpu_diffuse, oracle_diffuse,
+                         require_gpu, say)
+from structured_grid_cfd_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+DT = {"f64": np.float64, "f32": np.float32}
+NX, NY = 650, 520
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _gpu():
+    require_gpu()
+
+
+def _signed(dt, seed, scale_exp):
+    """Interior uniform [-1, 1) times 2**scale_exp (an exact scaling)."""
+    u, v = inputs.uniform_grid(NX, NY, seed, DT[dt])
+    w = u.copy()
+    w[1:-1, 1:NX - 1] = np.ldexp(u[1:-1, 1:NX - 1] * 2 - 1, scale_exp).astype(DT[dt])
+    return w, v
+
+
+def _run(u, v, steps, tb, rows, what, nan_ok=False):
+    say(what, u.dtype, tb, rows, steps)
+    got, in_v, _, _ = gpu_diffuse(u, v, NX, 0.1, steps, "temporal", tb, rows)
+    ref, ref_in_v = oracle_diffuse(u, v, NX, 0.1, steps)
+    assert in_v == ref_in_v
+    (assert_bitwise_nan if nan_ok else assert_bitwise)(got[:, :NX], ref[:, :NX], what)
+    return ref
+
+
+@pytest.mark.parametrize("rows", [0, 16])
+@pytest.mark.parametrize("tb", [2, 5, 8, 10, 12])
+@pytest.mark.parametrize("dt", ["f64", "f32"])
+def test_interior_tiles(dt, tb, rows):
+    u, v = inputs.uniform_grid(NX, NY, 71, DT[dt])
+    _run(u, v, 2 * tb + 3, tb, rows, "interior")
+
+
+@pytest.mark.parametrize("dt,exp", [("f64", 1000), ("f64", -1000), ("f64", -1070),
+                                    ("f32", 105), ("f32", -120), ("f32", -140)])
+def test_extreme_magnitudes(dt, exp):
+    """Signed values scaled to 2**exp: close to the largest inputs the fused
+    form takes at depth 8 (2**1000 in FP64 and 2**105 in FP32 pass the check),
+    and deep into the subnormal range, where 4c must still be exact."""
+    u, v = _signed(dt, 72, exp)
+    _run(u, v, 16, 8, 16, f"2^{exp}")
+
+
+@pytest.mark.parametrize("dt", ["f64", "f32"])
+@pytest.mark.parametrize("kind", ["overflow", "nan", "inf"])
+def test_fallback_cells(dt, kind):
+    """A cell whose 4c overflows (centre 2**(emax-1), neighbours half that:
+    the separate form gives -inf where the fused one stays finite), a NaN, or
+    an infinity, placed in an interior tile: the tile must be recomputed in
+    the separate form."""
+    u, v = inputs.uniform_grid(NX, NY, 73, DT[dt])
+    j, i = NY // 2, NX // 2
+    big = np.ldexp(1.0, 1022 if dt == "f64" else 126)
+    if kind == "overflow":
+        u[j, i] = big
+        u[j, i - 1] = u[j, i + 1] = u[j - 1, i] = u[j + 1, i] = big / 2
+    elif kind == "nan":
+        u[j, i] = np.nan
+    else:
+        u[j, i] = -np.inf
+    for tb, rows in [(8, 16), (5, 0), (12, 24)]:
+        ref = _run(u, v, 2 * tb, tb, rows, f"fallback {kind}", nan_ok=True)
+        assert not np.isfinite(ref).all()
