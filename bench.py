@@ -44,10 +44,12 @@ sys.path.insert(0, str(ROOT))
 
 METRIC = "cell-var updates/s and achieved HBM GB/s (% of MI355X peak), 1 GPU"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
-# Vector ALU peak for the stencil's plain (non-fused, non-packed) adds and
-# multiplies: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = 39.3 T operations/s in
-# FP32 or FP64 (the published 78.6 TFLOP/s FP64 counts an FMA as two).
-ALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
+# Vector ALU peak for the stencil's adds and multiplies, from the published
+# vector rates (an FMA counts as two operations there, one here):
+#   FP64 78.6 TFLOP/s = 256 CUs x 64 lanes x 2 x 2.4 GHz -> 39.3 T operations/s,
+#   FP32 157.3 TFLOP/s = 256 CUs x 128 lanes x 2 x 2.4 GHz -> 78.6 T operations/s
+# (plain FP32 adds and multiplies issue faster than FP64 ones on gfx950).
+ALU_PEAK_TOPS = {"f64": 256 * 64 * 2.4e9 / 1e12, "f32": 256 * 128 * 2.4e9 / 1e12}
 FLOPS_PER_UPDATE = 7  # W+E, +S, +N, 4*C, -, alpha*t, C+
 PROFILE_COUNTERS = ROOT / "profiles" / "diffusion_march_counters.json"
 
@@ -152,7 +154,8 @@ def main():
     sweeps_per_launch = sweeps / launches
     hbm_gbs = bytes_per_launch / avg_launch_s / 1e9
     alu_tops = FLOPS_PER_UPDATE * (nx - 2) * (ny - 2) * sweeps_per_launch / avg_launch_s / 1e12
-    hbm_frac, alu_frac = hbm_gbs / HBM_PEAK_GBS, alu_tops / ALU_PEAK_TOPS
+    alu_peak = ALU_PEAK_TOPS[args.dtype]
+    hbm_frac, alu_frac = hbm_gbs / HBM_PEAK_GBS, alu_tops / alu_peak
     traffic = None
     if PROFILE_COUNTERS.exists():
         prof = json.loads(PROFILE_COUNTERS.read_text())
@@ -165,7 +168,7 @@ def main():
         roofline = {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(hbm_frac, 4), "traffic": traffic}
     else:
-        roofline = {"bound": "alu", "achieved": round(alu_tops, 2), "peak": round(ALU_PEAK_TOPS, 2),
+        roofline = {"bound": "alu", "achieved": round(alu_tops, 2), "peak": round(alu_peak, 2),
                     "unit": "TFLOP/s", "frac": round(alu_frac, 4), "traffic": traffic}
     roofline.update({"kernel": kernel_name, "avg_launch_us": round(avg_launch_s * 1e6, 3),
                      "launches_timed": n_launch, "bytes_per_launch": bytes_per_launch,
