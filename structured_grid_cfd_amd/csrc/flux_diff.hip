@@ -14,11 +14,12 @@
 //     inside (the page's "after");
 //   * TILED -- one thread per (j, k) column marching a run of l planes: the
 //     high z face of plane l is kept in a register as the low face of plane
-//     l+1, so every face is read from memory once; 1/dx and 1/dy are formed
-//     once per column and 1/dz once per plane per workgroup (in LDS); the
-//     variables advance in groups of four so each plane step has twenty
-//     independent loads in flight.  The 2D form marches along k instead,
-//     treating Fy as the marched face.
+//     l+1; 1/dx and 1/dy are formed once per column and 1/dz once per plane
+//     per workgroup (in LDS).  Each workgroup handles one variable and the
+//     workgroups are ordered variable-major, so at any time the chip streams
+//     the five arrays of about one variable: streaming many arrays at once
+//     (all variables per thread) measured 10-13% slower on MI355X.  The 2D
+//     form marches along k instead, treating Fy as the marched face.
 #include "sgc_internal.h"
 
 namespace sgc {
@@ -102,20 +103,24 @@ struct PencilArgs {
     int nxv, nyv, nzv;
     int planes;       // planes per workgroup run
     int col_blocks;   // workgroups across the nxv*nyv columns
+    int runs;         // plane runs along the marched axis
+    int per_var;      // workgroups per variable (a multiple of 8)
 };
 
-// Variables are marched in groups of VG: per plane step a thread issues the
-// 5*VG face loads of the group at once, which is what keeps enough bytes in
-// flight with only a few thousand waves.
-constexpr int kVarGroup = 4;
 
 template <bool HAS_Y>
 __global__ __launch_bounds__(256) void k_flux_pencil(PencilArgs a) {
     __shared__ double iz_s[kMaxPlanes];
     const FluxArgs &g = a.g;
-    const int b = xcd_remap(blockIdx.x, gridDim.x);
-    const int cb = b % a.col_blocks;
-    const int lb = b / a.col_blocks;
+    // Variable-major block order, dispatched as is: the resident blocks of
+    // every XCD work on one variable's arrays at a time.
+    const int per_var = a.per_var;  // col_blocks * runs rounded up to a multiple of 8
+    const int b = blockIdx.x;
+    const int v = b / per_var;
+    const int rem = xcd_remap(b - v * per_var, per_var);
+    if (rem >= a.col_blocks * a.runs) return;
+    const int lb = rem / a.col_blocks;
+    const int cb = rem - lb * a.col_blocks;
     const int l0 = lb * a.planes;
     const int l1 = min(l0 + a.planes, a.nzv);
     const double *__restrict__ dzv = HAS_Y ? g.dz : g.dy;
@@ -133,54 +138,33 @@ __global__ __launch_bounds__(256) void k_flux_pencil(PencilArgs a) {
     const int sc = ncols;                // cell / marched-face plane size
     const int n = sc * a.nzv;
     const int ox = c + k;                // j + (nxv+1)*k
-    constexpr int VG = kVarGroup;
-    for (int v0 = 0; v0 < g.nvar; v0 += VG) {
-        // Members past the last variable repeat it: they load the same faces
-        // and store the same bits to the same cells from the same thread, which
-        // keeps the loop free of branches around its loads.
-        const double *__restrict__ FX[VG];
-        const double *__restrict__ FY[VG];
-        const double *__restrict__ FZ[VG];
-        double *__restrict__ R[VG];
-#pragma unroll
-        for (int u = 0; u < VG; ++u) {
-            const int v = min(v0 + u, g.nvar - 1);
-            FX[u] = g.fx.p[v];
-            FY[u] = g.fy.p[v];
-            FZ[u] = HAS_Y ? g.fz.p[v] : g.fy.p[v];
-            R[u] = g.rhs + (long)v * n;
+    const double *__restrict__ FX = g.fx.p[v];
+    const double *__restrict__ FY = g.fy.p[v];
+    const double *__restrict__ FZ = HAS_Y ? g.fz.p[v] : g.fy.p[v];
+    double *__restrict__ R = g.rhs + (long)v * n;
+    double zlo = FZ[c + sc * l0];
+    for (int l = l0; l < l1; ++l) {
+        const double xl = FX[ox + sx * l];
+        const double xh = FX[ox + sx * l + 1];
+        double yl = 0.0, yh = 0.0;
+        if (HAS_Y) {
+            yl = FY[c + sy * l];
+            yh = FY[c + sy * l + a.nxv];
         }
-        double zlo[VG];
-#pragma unroll
-        for (int u = 0; u < VG; ++u) zlo[u] = FZ[u][c + sc * l0];
-        for (int l = l0; l < l1; ++l) {
-            double xl[VG], xh[VG], yl[VG], yh[VG], zh[VG];
-#pragma unroll
-            for (int u = 0; u < VG; ++u) {
-                xl[u] = FX[u][ox + sx * l];
-                xh[u] = FX[u][ox + sx * l + 1];
-                if (HAS_Y) {
-                    yl[u] = FY[u][c + sy * l];
-                    yh[u] = FY[u][c + sy * l + a.nxv];
-                }
-                zh[u] = FZ[u][c + sc * (l + 1)];
-            }
-            const double iz = iz_s[l - l0];
-#pragma unroll
-            for (int u = 0; u < VG; ++u) {
-                double r = face_term(xl[u], xh[u], ix);
-                if (HAS_Y) r = add(r, face_term(yl[u], yh[u], iy));
-                r = add(r, face_term(zlo[u], zh[u], iz));
-                R[u][c + sc * l] = r;
-                zlo[u] = zh[u];
-            }
-        }
+        const double zh = FZ[c + sc * (l + 1)];
+        double r = face_term(xl, xh, ix);
+        if (HAS_Y) r = add(r, face_term(yl, yh, iy));
+        r = add(r, face_term(zlo, zh, iz_s[l - l0]));
+        R[c + sc * l] = r;
+        zlo = zh;
     }
 }
 
 // Waves over the grid: the plane run per thread is chosen so the launch has
-// about this many (16k measured best: more waves, more loads in flight).
-constexpr int kTargetWaves = 16384;
+// about this many, which in practice means the shortest runs (two planes) on
+// the grids measured: more waves, more loads in flight, and the z faces of a
+// run boundary are the only ones read twice.
+constexpr int kTargetWaves = 262144;
 
 }  // namespace
 
@@ -224,14 +208,16 @@ int flux_launch(const PtrTable &fx, const PtrTable &fy, const PtrTable *fz, cons
     const long ncols = (long)a.nxv * a.nyv;
     a.col_blocks = (int)((ncols + 255) / 256);
     const long waves_per_run = (ncols + 63) / 64;
-    long runs = (kTargetWaves + waves_per_run - 1) / waves_per_run;
+    long runs = (kTargetWaves + waves_per_run * nvar - 1) / (waves_per_run * nvar);
     if (runs < 1) runs = 1;
     int planes = (int)((a.nzv + runs - 1) / runs);
     planes = planes < 2 ? 2 : planes;
     planes = planes > kMaxPlanes ? kMaxPlanes : planes;
     planes = planes > a.nzv ? a.nzv : planes;
     a.planes = planes;
-    const long blocks = (long)a.col_blocks * ((a.nzv + planes - 1) / planes);
+    a.runs = (a.nzv + planes - 1) / planes;
+    a.per_var = ((a.col_blocks * a.runs + 7) / 8) * 8;
+    const long blocks = (long)a.per_var * nvar;
     if (has_z) hipLaunchKernelGGL((k_flux_pencil<true>), dim3((unsigned)blocks), dim3(256), 0, s, a);
     else hipLaunchKernelGGL((k_flux_pencil<false>), dim3((unsigned)blocks), dim3(256), 0, s, a);
     return check_launch("flux difference, column pencils");
