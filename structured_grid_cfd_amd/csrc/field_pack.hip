@@ -86,9 +86,11 @@ constexpr int kChunkVec = 4 * 256;
 template <bool UNPACK>
 __global__ __launch_bounds__(256) void k_copy(PackArgs g, int chunks_per_var) {
     typedef double d2 __attribute__((ext_vector_type(2)));
-    const int b = xcd_remap(blockIdx.x, gridDim.x);
-    const int v = b / chunks_per_var;
-    const int chunk = b - v * chunks_per_var;
+    // Variable-major: all XCDs copy one variable at a time, each a contiguous
+    // range of its chunks (chunks_per_var is a multiple of 8; chunks past the
+    // variable's end copy nothing).
+    const int v = blockIdx.x / chunks_per_var;
+    const int chunk = xcd_remap(blockIdx.x - v * chunks_per_var, chunks_per_var);
     const int n = g.nx * g.ny * g.nz;
     const double *__restrict__ src = UNPACK ? g.packed + (long)v * n : g.f.p[v];
     double *__restrict__ dst = UNPACK ? const_cast<double *>(g.f.p[v]) : g.out + (long)v * n;
@@ -163,18 +165,22 @@ struct TransArgs {
     int p_in, p_out;   // plane offsets on each side
     int v_in, v_out;   // variable offsets on the packed side
     int nvar;
+    int per_var;       // workgroups per variable (tiles rounded up to a multiple of 8)
 };
 
 template <bool UNPACK>
 __global__ __launch_bounds__(256) void k_transpose(TransArgs g) {
     __shared__ double tile[64][65];
-    int t = xcd_remap(blockIdx.x, gridDim.x);
+    // Variable-major: all XCDs work on one variable's planes at a time, each
+    // on a contiguous range of its tiles.
+    const int per_var = g.per_var;  // ntx * nty * P rounded up to a multiple of 8
+    const int v = blockIdx.x / per_var;
+    int t = xcd_remap(blockIdx.x - v * per_var, per_var);
+    if (t >= g.ntx * g.nty * g.P) return;  // padding workgroup (uniform exit, before the barrier)
     const int tx = t % g.ntx;
     t /= g.ntx;
     const int ty = t % g.nty;
-    t /= g.nty;
-    const int p = t % g.P;
-    const int v = t / g.P;
+    const int p = t / g.nty;
     const int x0 = tx * g.TX, y0 = ty * g.TY;
     const int w = min(g.TX, g.X - x0), h = min(g.TY, g.Y - y0);
     const double *in = (UNPACK ? g.packed + v * g.v_in : g.f.p[v]) + p * g.p_in + x0 + y0 * g.s_in;
@@ -259,8 +265,10 @@ int launch_transpose(const PackArgs &a, Layout lay, hipStream_t s) {
     g.TY = balanced_tile(g.Y);
     g.ntx = (g.X + g.TX - 1) / g.TX;
     g.nty = (g.Y + g.TY - 1) / g.TY;
-    const long tiles = (long)g.ntx * g.nty * g.P * g.nvar;
+    const long per_var = (((long)g.ntx * g.nty * g.P + 7) / 8) * 8;
+    const long tiles = per_var * g.nvar;
     if (tiles > 0x7fffffffL) return fail(SGC_ERANGE, "transpose grid too large");
+    g.per_var = (int)per_var;
     hipLaunchKernelGGL((k_transpose<UNPACK>), dim3((unsigned)tiles), dim3(256), 0, s, g);
     return check_launch("pack transpose");
 }
@@ -285,7 +293,8 @@ int launch_pack(const PackArgs &g, int dir, int map, hipStream_t s) {
     if (map == SGC_VAR_TILED) {
         const Layout lay = tiled_layout(dir, g.nx, g.ny, g.nz);
         if (lay == Layout::Copy) {
-            const long per_var = ((long)n + 2L * kChunkVec - 1) / (2L * kChunkVec);
+            const long chunks = ((long)n + 2L * kChunkVec - 1) / (2L * kChunkVec);
+            const long per_var = ((chunks + 7) / 8) * 8;  // a multiple of 8 for the XCD remap
             const long blocks = per_var * g.nvar;
             if (blocks > 0x7fffffffL) return fail(SGC_ERANGE, "copy grid too large");
             hipLaunchKernelGGL((k_copy<UNPACK>), dim3((unsigned)blocks), dim3(256), 0, s, g, (int)per_var);
