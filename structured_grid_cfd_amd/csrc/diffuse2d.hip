@@ -550,8 +550,10 @@ int launch_march_kv(const void *src, void *dst, const DiffPlan &p, double alpha,
                       : k_march<T, TS, KV, false, kLoadPolicy, kStorePolicy>;
     long rows = p.tile_rows;
     if (rows <= 0) {
-        if (TS <= 3) {
-            rows = 8;  // memory bound: many short tiles in flight
+        if (TS <= 2) {
+            rows = 4;  // memory bound: many short tiles in flight
+        } else if (TS == 3) {
+            rows = 8;
         } else if (TS == 4) {
             // Between memory and ALU bound: about 8192 tiles of 16 to 128 rows.
             rows = max(16L, min((long)p.ny * g.nstrips / 8192, 128L));
