@@ -170,6 +170,11 @@ def main():
     else:
         roofline = {"bound": "alu", "achieved": round(alu_tops, 2), "peak": round(alu_peak, 2),
                     "unit": "TFLOP/s", "frac": round(alu_frac, 4), "traffic": traffic}
+    # The single-sweep bound: a kernel that reads the grid and writes it once
+    # per sweep can do at most HBM peak / (bytes per cell per sweep) updates/s.
+    single_sweep_bound = HBM_PEAK_GBS * 1e9 / (2 * es)
+    roofline.update({"single_sweep_hbm_bound_cu_s": single_sweep_bound,
+                     "value_over_single_sweep_bound": round(value / single_sweep_bound, 3)})
     roofline.update({"kernel": kernel_name, "avg_launch_us": round(avg_launch_s * 1e6, 3),
                      "launches_timed": n_launch, "bytes_per_launch": bytes_per_launch,
                      "hbm_gbs": round(hbm_gbs, 1), "hbm_frac": round(hbm_frac, 4),
