@@ -47,7 +47,8 @@ typedef enum sgc_status {
     SGC_ENULL = 2,  /* a required pointer (or pointer-table entry) is NULL   */
     SGC_EDTYPE = 3, /* unknown dtype code                                    */
     SGC_EALIAS = 4, /* an output overlaps an input or the other buffer       */
-    SGC_ERANGE = 5, /* an array exceeds 2^31 - 1 elements, or time_block > max */
+    SGC_ERANGE = 5, /* an array exceeds 2^31 - 1 elements, time_block > max, or
+                       a row too long for the marching maps (see below)         */
     SGC_EHIP = 6    /* the HIP runtime refused a launch (message has details) */
 } sgc_status;
 
@@ -104,7 +105,11 @@ typedef enum sgc_dir { SGC_DIR_X = 0, SGC_DIR_Y = 1, SGC_DIR_Z = 2 } sgc_dir;
  *               SGC_MAX_TIME_BLOCK (SGC_ERANGE above); ignored by other maps.
  *   tile_rows   rows per wave tile for SGC_DIFF_TILED / SGC_DIFF_TEMPORAL;
  *               0 chooses automatically; otherwise 1 .. ny.  Ignored by the
- *               other maps.
+ *               other maps.  The marching maps address each wave's rows
+ *               through a window of 2^30 bytes, so tiles are at most
+ *               2^30 / (ld * element size) - 2*time_block - 8 rows; where that
+ *               is below 1 (rows of ~45 MB or more) they return SGC_ERANGE
+ *               before enqueueing anything, and the page maps still apply.
  *   stream      hipStream_t or NULL.
  *   result_is_v optional out (host): 1 if the result is in v, 0 if in u.
  *
