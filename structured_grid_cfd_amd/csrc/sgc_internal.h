@@ -40,15 +40,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
                                              0x00020000);
 }
-// POL: cache policy bits (2 = non-temporal: the line is not expected to be
-// re-read, which streams it past the caches).
+// POL: cache policy bits of gfx950 buffer instructions (1 = sc0, 2 = nt:
+// the line is not expected to be re-read, 16 = sc1).
 template <int POL = 0>
 __device__ __forceinline__ double buf_load_f64(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(double, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, POL));
 }
+template <int POL = 0>
 __device__ __forceinline__ void buf_store_f64(double x, __amdgpu_buffer_rsrc_t r, uint32_t off) {
     typedef int i32x2 __attribute__((ext_vector_type(2)));
-    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, x), r, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, x), r, off, 0, POL);
 }
 
 // ---- diffusion (diffuse2d.hip) --------------------------------------------
