@@ -315,7 +315,8 @@ def measure_all(log) -> dict:
         del u, v, u0, v0
         torch.cuda.empty_cache()
 
-    # 64x64 impulse, 32 sweeps: launch/latency bound
+    # 64x64 impulse, 32 sweeps: launch/latency bound (production march, and the
+    # resident map that runs all sweeps in one workgroup)
     c = inputs.cfg1()
     u, v = dev(c["u"]), dev(c["v"])
     cfg = launch_config.diffusion("f64")
@@ -323,6 +324,9 @@ def measure_all(log) -> dict:
                                                 0, stream), 10, False)
     res["diffusion_64_f64_32sweeps"] = entry(t, 62 * 62 * 32, (64 * 64 + 62 * 62) * 8 *
                                              binding.stencil_diffuse2d_launches(32, cfg["map"], cfg["time_block"]))
+    t = timed(lambda: binding.stencil_diffuse2d(u, v, 64, 0.1, 32, "resident", 1, 0, stream), 10, False)
+    res["diffusion_64_f64_32sweeps_resident"] = entry(t, 62 * 62 * 32, (64 * 64 + 62 * 62) * 8,
+                                                      {"map": "resident", "launches": 1})
 
     # 16384^2 FP32, 200 sweeps
     c = inputs.cfg5_diffusion()

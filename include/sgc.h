@@ -66,10 +66,13 @@ typedef enum sgc_diff_map {
     SGC_DIFF_TILED = 3,           /* one step per launch: each wave marches a
                                      column strip along j with 16-byte row loads
                                      and a three-row register window            */
-    SGC_DIFF_TEMPORAL = 4         /* time_block steps per launch: the march
+    SGC_DIFF_TEMPORAL = 4,        /* time_block steps per launch: the march
                                      keeps one window per time level and
                                      recomputes the halo, one HBM read and
                                      write per launch                           */
+    SGC_DIFF_RESIDENT = 5         /* small grids (nx <= 64, ny <= 128): one
+                                     workgroup holds the grid in registers and
+                                     runs every step in a single launch         */
 } sgc_diff_map;
 
 /* Variable-loop mappings of the per-variable field kernels ([MFC] Changes and
@@ -112,6 +115,11 @@ typedef enum sgc_dir { SGC_DIR_X = 0, SGC_DIR_Y = 1, SGC_DIR_Z = 2 } sgc_dir;
  *               before enqueueing anything, and the page maps still apply.
  *   stream      hipStream_t or NULL.
  *   result_is_v optional out (host): 1 if the result is in v, 0 if in u.
+ *
+ * SGC_DIFF_RESIDENT returns SGC_ERANGE for grids wider than 64 or taller
+ * than 128 cells, or for more than 2^31 - 1 steps, before enqueueing
+ * anything; it leaves the state one step before the result in the other
+ * buffer.
  *
  * Semantics: the edge ring (i = 0, nx-1 or j = 0, ny-1) is treated as 0 in
  * both buffers whatever the caller stored there, and the result buffer's ring

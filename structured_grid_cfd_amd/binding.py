@@ -26,7 +26,8 @@ PKG = Path(__file__).resolve().parent
 LIB_PATH = PKG / "libsgc.so"
 HEADER = PKG.parent / "include" / "sgc.h"
 
-DIFF_MAPS = {"collapse_branch": 0, "contig": 1, "strided": 2, "tiled": 3, "temporal": 4}
+DIFF_MAPS = {"collapse_branch": 0, "contig": 1, "strided": 2, "tiled": 3, "temporal": 4,
+             "resident": 5}
 VAR_MAPS = {"per_cell": 0, "per_cellvar": 1, "tiled": 2}
 DIRS = {"x": 0, "y": 1, "z": 2, 0: 0, 1: 1, 2: 2}
 STATUS = {0: "SGC_OK", 1: "SGC_EINVAL", 2: "SGC_ENULL", 3: "SGC_EDTYPE", 4: "SGC_EALIAS",

@@ -110,6 +110,8 @@ int64_t stencil_diffuse2d_launches(int64_t steps, int32_t map, int32_t time_bloc
     case SGC_DIFF_TEMPORAL:
         if (time_block < 1 || time_block > SGC_MAX_TIME_BLOCK) return -1;
         return temporal_launches(steps, time_block);
+    case SGC_DIFF_RESIDENT:
+        return steps > 0 ? 1 : 0;
     default:
         return -1;
     }
@@ -126,7 +128,7 @@ int stencil_diffuse2d(void *u, void *v, int32_t dtype, int64_t nx, int64_t ny, i
     if (ld < nx) return fail(SGC_EINVAL, "stencil_diffuse2d: ld must be >= nx");
     if (steps < 0) return fail(SGC_EINVAL, "stencil_diffuse2d: steps must be >= 0");
     if (!std::isfinite(alpha)) return fail(SGC_EINVAL, "stencil_diffuse2d: alpha must be finite");
-    if (map < SGC_DIFF_COLLAPSE_BRANCH || map > SGC_DIFF_TEMPORAL)
+    if (map < SGC_DIFF_COLLAPSE_BRANCH || map > SGC_DIFF_RESIDENT)
         return fail(SGC_EINVAL, fmt("stencil_diffuse2d: unknown map %lld", map));
     if (map == SGC_DIFF_TEMPORAL) {
         if (time_block < 1) return fail(SGC_EINVAL, "stencil_diffuse2d: time_block must be >= 1");
@@ -160,6 +162,11 @@ int stencil_diffuse2d(void *u, void *v, int32_t dtype, int64_t nx, int64_t ny, i
             rc = diffuse_sweep(odd ? u : v, odd ? v : u, dtype, p, alpha, map, 1, s);
             if (rc) return rc;
         }
+    } else if (map == SGC_DIFF_RESIDENT) {
+        if (steps > 0x7fffffffLL) return fail(SGC_ERANGE, "stencil_diffuse2d: resident sweep takes at most 2^31-1 steps");
+        const bool odd = (steps & 1) != 0;
+        rc = diffuse_resident(u, odd ? v : u, odd ? u : v, dtype, p, alpha, (int)steps, s);
+        if (rc) return rc;
     } else if (map == SGC_DIFF_TILED) {
         // The march treats the ring as 0 on read and writes it as 0.
         for (int64_t k = 1; k <= steps; ++k) {

@@ -424,6 +424,75 @@ __global__ __launch_bounds__(256) void k_march(MarchArgs g) {
 }
 
 // ---------------------------------------------------------------------------
+// Resident sweep for small grids: every step in one launch
+// ---------------------------------------------------------------------------
+
+// A grid of at most 64 columns and 16*R rows lives in the registers of one
+// workgroup of sixteen waves: lane i holds column i, wave w holds rows
+// [w*R, w*R + R).  West/east neighbours cross lanes with DPP; north/south
+// come from the lane's own rows, except at a wave's first and last row, whose
+// neighbours are the adjacent waves' last and first rows: each step every
+// wave publishes those two rows in LDS (two slot sets used alternately, so
+// one barrier per step suffices) and reads its neighbours'.  Ring cells and
+// cells outside the grid hold 0 and are never updated.  On return `dst`
+// holds the state after `steps` steps and `prev` the state one step earlier,
+// as alternating sweeps would leave them; both include the zero ring.
+// `src` may equal `dst` or `prev`: all reads of `src` precede the first
+// barrier, all writes follow it.
+constexpr int kResidentWaves = 16;
+constexpr int kResidentCols = 64;
+
+template <typename T, int R>
+__global__ __launch_bounds__(1024) void k_resident(const T *src, T *dst, T *prev, int nx, int ny,
+                                                   int ld, T a, int steps) {
+    __shared__ T edge[2][kResidentWaves][2][kResidentCols];  // [slot set][wave][first, last row][lane]
+    const int i = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int j0 = w * R;
+    const bool colin = i >= 1 && i <= nx - 2;
+    T val[R];
+    bool upd[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int j = j0 + r;
+        upd[r] = colin && j >= 1 && j <= ny - 2;
+        val[r] = upd[r] ? src[i + (long)ld * j] : T(0);
+    }
+    for (int s = 0; s < steps; ++s) {
+        const int set = s & 1;
+        edge[set][w][0][i] = val[0];
+        edge[set][w][1][i] = val[R - 1];
+        __syncthreads();
+        const T below = w > 0 ? edge[set][w - 1][1][i] : T(0);                   // row j0 - 1
+        const T above = w < kResidentWaves - 1 ? edge[set][w + 1][0][i] : T(0);  // row j0 + R
+        if (s == steps - 1) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int j = j0 + r;
+                if (i < nx && j < ny) prev[i + (long)ld * j] = val[r];
+            }
+        }
+        T nv[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const T c = val[r];
+            const T west = wave_shr1(c);
+            const T east = wave_shl1(c);
+            const T south = r == 0 ? below : val[r - 1];
+            const T north = r == R - 1 ? above : val[r + 1];
+            nv[r] = upd[r] ? five_point(west, east, south, north, c, a) : T(0);
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) val[r] = nv[r];
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int j = j0 + r;
+        if (i < nx && j < ny) dst[i + (long)ld * j] = val[r];
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Host-side launch selection
 // ---------------------------------------------------------------------------
 
@@ -636,6 +705,28 @@ int diffuse_zero_ring(void *buf, int dtype, int nx, int ny, int ld, hipStream_t 
         hipLaunchKernelGGL((k_zero_ring<float>), grid, dim3(256), 0, s, static_cast<float *>(buf), nx,
                            ny, ld);
     return check_launch("edge-ring zeroing");
+}
+
+template <typename T>
+int resident_t(const void *src, void *dst, void *prev, const DiffPlan &p, double alpha, int steps,
+               hipStream_t s) {
+    const T *in = static_cast<const T *>(src);
+    T *out = static_cast<T *>(dst);
+    T *before = static_cast<T *>(prev);
+    const T a = T(alpha);
+    if (p.ny <= kResidentWaves * 4)
+        hipLaunchKernelGGL((k_resident<T, 4>), dim3(1), dim3(1024), 0, s, in, out, before, p.nx, p.ny, p.ld, a, steps);
+    else
+        hipLaunchKernelGGL((k_resident<T, 8>), dim3(1), dim3(1024), 0, s, in, out, before, p.nx, p.ny, p.ld, a, steps);
+    return check_launch("diffusion resident sweep");
+}
+
+int diffuse_resident(const void *src, void *dst, void *prev, int dtype, const DiffPlan &p, double alpha,
+                     int steps, hipStream_t s) {
+    if (p.nx > kResidentCols || p.ny > kResidentWaves * 8)
+        return fail(SGC_ERANGE, "resident sweep: the grid must fit 64 columns and 128 rows");
+    if (dtype == SGC_F64) return resident_t<double>(src, dst, prev, p, alpha, steps, s);
+    return resident_t<float>(src, dst, prev, p, alpha, steps, s);
 }
 
 int diffuse_sweep(const void *src, void *dst, int dtype, const DiffPlan &p, double alpha, int map,

@@ -59,6 +59,10 @@ struct DiffPlan {
     int tile_rows;   // 0 = automatic
 };
 int diffuse_zero_ring(void *buf, int dtype, int nx, int ny, int ld, hipStream_t s);
+// All `steps` steps of a grid of at most 64 x 128 cells in one launch: the
+// result in dst, the state one step earlier in prev (SGC_ERANGE if larger).
+int diffuse_resident(const void *src, void *dst, void *prev, int dtype, const DiffPlan &p,
+                     double alpha, int steps, hipStream_t s);
 int diffuse_sweep(const void *src, void *dst, int dtype, const DiffPlan &p,
                   double alpha, int map, int steps_in_launch, hipStream_t s);
 

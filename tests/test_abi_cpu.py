@@ -57,6 +57,8 @@ def test_temporal_launch_count_parity(lib, steps, tb, expect):
 def test_launch_count_other_maps(lib):
     for m in ("collapse_branch", "contig", "strided", "tiled"):
         assert b.stencil_diffuse2d_launches(17, m, 99) == 17
+    assert b.stencil_diffuse2d_launches(17, "resident", 99) == 1
+    assert b.stencil_diffuse2d_launches(0, "resident", 1) == 0
     assert b.stencil_diffuse2d_launches(-1, "tiled", 1) == -1
     assert b.stencil_diffuse2d_launches(5, "temporal", 0) == -1
     assert b.stencil_diffuse2d_launches(5, "temporal", 13) == -1
@@ -75,12 +77,15 @@ U, V = 0x10000, 0x90000  # fake, never dereferenced: every call below fails vali
     ((U, V, 1, 8, 8, 8, 0.1, -1, 3, 1, 0), 1, "steps"),
     ((U, V, 1, 8, 8, 8, float("nan"), 1, 3, 1, 0), 1, "finite"),
     ((U, V, 1, 8, 8, 8, float("inf"), 1, 3, 1, 0), 1, "finite"),
-    ((U, V, 1, 8, 8, 8, 0.1, 1, 5, 1, 0), 1, "map"),
+    ((U, V, 1, 8, 8, 8, 0.1, 1, 6, 1, 0), 1, "map"),
     ((U, V, 1, 8, 8, 8, 0.1, 1, 4, 0, 0), 1, "time_block"),
     ((U, V, 1, 8, 8, 8, 0.1, 1, 4, 13, 0), 5, "time_block"),
     ((U, V, 1, 8, 8, 8, 0.1, 1, 3, 1, 9), 1, "tile_rows"),
     ((U, V, 1, 8, 8, 8, 0.1, 1, 3, 1, -1), 1, "tile_rows"),
     ((U, V, 1, 70000, 70000, 70000, 0.1, 1, 3, 1, 0), 5, "2^31"),
+    ((U, V, 1, 65, 8, 65, 0.1, 1, 5, 1, 0), 5, "64 columns"),
+    ((U, V, 1, 8, 129, 8, 0.1, 1, 5, 1, 0), 5, "128 rows"),
+    ((U, V, 1, 8, 8, 8, 0.1, 1 << 31, 5, 1, 0), 5, "2^31-1 steps"),
     ((U, U + 8 * 63, 1, 8, 8, 8, 0.1, 1, 3, 1, 0), 4, "overlap"),
     ((U + 4, V, 1, 8, 8, 8, 0.1, 1, 3, 1, 0), 1, "aligned"),
     ((U, V + 2, 0, 8, 8, 8, 0.1, 1, 3, 1, 0), 1, "aligned"),

@@ -20,7 +20,7 @@ from structured_grid_cfd_amd import binding, inputs
 pytestmark = pytest.mark.gpu
 
 PAGE_MAPS = ["collapse_branch", "contig", "strided"]
-ALL_MAPS = [(m, 1) for m in PAGE_MAPS + ["tiled"]] + [("temporal", t) for t in range(1, 13)]
+ALL_MAPS = [(m, 1) for m in PAGE_MAPS + ["tiled", "resident"]] + [("temporal", t) for t in range(1, 13)]
 DT = {"f64": np.float64, "f32": np.float32}
 
 
@@ -52,7 +52,7 @@ def test_impulse_64x64_32_steps(m, tb, dt):
 
 
 @pytest.mark.parametrize("steps", [7, 8, 31, 32])
-@pytest.mark.parametrize("m,tb", [(m, 1) for m in PAGE_MAPS + ["tiled"]] + [("temporal", 4), ("temporal", 12)])
+@pytest.mark.parametrize("m,tb", [(m, 1) for m in PAGE_MAPS + ["tiled", "resident"]] + [("temporal", 4), ("temporal", 12)])
 @pytest.mark.parametrize("dt", ["f64", "f32"])
 def test_page_validation_matrix_31x27(steps, m, tb, dt):
     u, v = inputs.page_impulse_grid(31, 27, DT[dt])
@@ -115,11 +115,13 @@ def test_dirty_input_edges_are_zeroed(dt):
     u0[:, 0] = -2
     u0[-1, :] = 3
     u0[:, nx - 1] = 7
+    u0[:, 59] = 7  # the east edge when the resident map runs the first 60 columns
     v0[:] = 11
     for m, tb in ALL_MAPS:
-        got = _check(u0, v0, nx, 0.1, 6, m, tb, what="dirty edges")
-        assert np.all(got[0, :] == 0) and np.all(got[:, 0] == 0)
-        assert np.all(got[-1, :] == 0) and np.all(got[:, nx - 1] == 0)
+        n = 60 if m == "resident" else nx  # the resident map takes at most 64 columns
+        got = _check(u0, v0, n, 0.1, 6, m, tb, what="dirty edges")
+        assert np.all(got[0, :n] == 0) and np.all(got[:, 0] == 0)
+        assert np.all(got[-1, :n] == 0) and np.all(got[:, n - 1] == 0)
 
 
 @pytest.mark.parametrize("dt", ["f64", "f32"])
@@ -131,6 +133,33 @@ def test_zero_steps(dt):
         assert not in_v
         ref, _ = oracle_diffuse(u0, v0, 33, 0.1, 0)
         assert_bitwise(got, ref, "zero steps")
+
+
+@pytest.mark.parametrize("nx,ny,ld", [(3, 3, 3), (5, 7, 8), (31, 27, 31), (64, 64, 64), (64, 128, 64),
+                                      (17, 100, 20), (64, 65, 70), (63, 128, 63), (40, 3, 40)])
+@pytest.mark.parametrize("steps", [1, 2, 7, 32, 33])
+@pytest.mark.parametrize("dt", ["f64", "f32"])
+def test_resident_small_grids(nx, ny, ld, steps, dt):
+    """One workgroup runs every step: the result is the oracle's, and the
+    other buffer holds the state one step earlier, as alternating sweeps
+    leave it (zero ring included); padding columns are untouched."""
+    u0, v0 = inputs.uniform_grid(nx, ny, 70 + nx + ny, DT[dt], ld=ld, pad_value=np.nan)
+    got = _check(u0, v0, nx, 0.1, steps, "resident", what=f"resident {nx}x{ny}")
+    _, in_v, uh, vh = gpu_diffuse(u0, v0, nx, 0.1, steps, "resident")
+    other = uh if in_v else vh
+    before, _ = oracle_diffuse(u0, v0, nx, 0.1, steps - 1)
+    assert_bitwise(other[:, :nx], before[:, :nx], "resident: previous state")
+    assert_bitwise(got[:, :nx], _check(u0, v0, nx, 0.1, steps, "temporal", 8)[:, :nx], "resident vs march")
+
+
+def test_resident_rejects_large_grids():
+    u = torch.zeros(129, 64, dtype=torch.float64, device="cuda")
+    v = torch.zeros_like(u)
+    with pytest.raises(binding.SGCError):
+        binding.stencil_diffuse2d(u, v, 64, 0.1, 4, "resident")
+    w = torch.zeros(10, 65, dtype=torch.float32, device="cuda")
+    with pytest.raises(binding.SGCError):
+        binding.stencil_diffuse2d(w, torch.zeros_like(w), 65, 0.1, 4, "resident")
 
 
 @pytest.mark.parametrize("alpha", [0.05, 0.25, 0.3, 1.0 / 3.0])
