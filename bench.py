@@ -64,8 +64,8 @@ def parse():
     p.add_argument("--tile-rows", type=int, default=None)
     p.add_argument("--quick", action="store_true", help="headline only: skip the per-kernel table")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    p.add_argument("--cpu-steps", type=int, default=400,
-                   help="sweeps of the CPU-baseline sample (same grid)")
+    p.add_argument("--cpu-steps", type=int, default=1000,
+                   help="sweeps of the CPU-baseline sample (same grid; 1000 = one full step, ~11 s)")
     p.add_argument("--ref-copy", action="store_true",
                    help="first run one 1 GiB copy (1 GiB read + 1 GiB written) as a known-size "
                         "reference for profiler byte counters")
@@ -191,8 +191,8 @@ def main():
         dt = time.perf_counter() - t
         cpu = {"value": (nx - 2) * (ny - 2) * args.cpu_steps / dt, "unit": "cell-var updates/s",
                "cores": 1, "kind": "oracle",
-               "sample": f"{nx}x{ny} {args.dtype}, {args.cpu_steps} of the {sweeps} sweeps, "
-                         f"single-threaded C oracle ({dt:.1f} s on {platform.processor() or 'host'}"
+               "sample": f"{nx}x{ny} {args.dtype}, {args.cpu_steps} of the {sweeps} sweeps of one "
+                         f"step, single-threaded C oracle ({dt:.1f} s on {platform.processor() or 'host'}"
                          f", {os.cpu_count()} host cores visible)"}
         log(f"cpu baseline: {cpu['value']:.4e} cell-updates/s in {dt:.1f} s")
 
