@@ -8,7 +8,8 @@
 //     section 5.1-5.3 (flattened grid with an edge branch; workgroup per row
 //     with lanes along i; workgroup per column with lanes along j);
 //   * k_march<T, TS, KV, ...> -- this library's sweep: one wave owns a strip
-//     of 64*K columns (K elements per lane = one 16-byte load) and marches up
+//     of 64*K columns (K = 2 elements per lane: one 16-byte FP64 or 8-byte
+//     FP32 load per lane and row) and marches up
 //     a tile of rows, keeping a three-row register window per time level.
 //     West/east neighbours cross lanes with DPP wave shifts, north/south come
 //     from the window, so every input row is read from memory exactly once and
@@ -117,15 +118,19 @@ __global__ __launch_bounds__(256) void k_zero_ring(T *__restrict__ g, int nx, in
 // Marching strip sweep with optional temporal blocking
 // ---------------------------------------------------------------------------
 
-// One 16-byte vector: V elements.
-template <typename T> struct Vec16;
-template <> struct Vec16<float> {
-    static constexpr int V = 4;
-    typedef float type __attribute__((ext_vector_type(4)));
-};
-template <> struct Vec16<double> {
-    static constexpr int V = 2;
-    typedef double type __attribute__((ext_vector_type(2)));
+// The vector one lane loads per row, VN elements.  FP64 uses two (16 bytes).
+// FP32 uses four (16 bytes) for one or two fused steps, which are memory
+// bound and stream better with 16-byte accesses, and two (8 bytes) for
+// deeper fusion: twice the strips means fewer row tiles for the same wave
+// count, and the taller tiles save more recomputed halo rows than the extra
+// halo columns cost (measured +3-8% at 4096^2..16384^2, +35% at 2048^2;
+// 8-byte vectors were 8-10% slower at one or two steps).
+template <typename T> constexpr int lane_elems(int ts) {
+    return sizeof(T) == 8 ? 2 : (ts <= 2 ? 4 : 2);
+}
+template <typename T, int VN> struct LaneVec {
+    static constexpr int V = VN;
+    typedef T type __attribute__((ext_vector_type(VN)));
 };
 
 // DPP wavefront shifts by one lane (GFX9 dpp_ctrl 0x138 wave_shr:1 and 0x130
@@ -156,13 +161,17 @@ __device__ __forceinline__ double wave_shl1(double x) {
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 
-// Loads 16 bytes into x[at .. at+V).
-template <int POL, typename T, int K>
+// Loads one VN-element lane vector into x[at .. at+VN).
+template <int POL, int VN, typename T, int K>
 __device__ __forceinline__ void buf_load_vec(T (&x)[K], int at, __amdgpu_buffer_rsrc_t r, uint32_t off) {
-    const i32x4 w = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, POL);
-    const typename Vec16<T>::type y = __builtin_bit_cast(typename Vec16<T>::type, w);
+    typedef typename LaneVec<T, VN>::type VT;
+    VT y;
+    if constexpr (sizeof(VT) == 16)
+        y = __builtin_bit_cast(VT, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, POL));
+    else
+        y = __builtin_bit_cast(VT, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, POL));
 #pragma unroll
-    for (int e = 0; e < Vec16<T>::V; ++e) x[at + e] = y[e];
+    for (int e = 0; e < VN; ++e) x[at + e] = y[e];
 }
 template <int POL>
 __device__ __forceinline__ float buf_load_elem(float *, __amdgpu_buffer_rsrc_t r, uint32_t off) {
@@ -172,13 +181,17 @@ template <int POL>
 __device__ __forceinline__ double buf_load_elem(double *, __amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(double, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, POL));
 }
-// Stores x[at .. at+V) as 16 bytes.
-template <int POL, typename T, int K>
+// Stores x[at .. at+VN) as one lane vector.
+template <int POL, int VN, typename T, int K>
 __device__ __forceinline__ void buf_store_vec(const T (&x)[K], int at, __amdgpu_buffer_rsrc_t r, uint32_t off) {
-    typename Vec16<T>::type y;
+    typedef typename LaneVec<T, VN>::type VT;
+    VT y;
 #pragma unroll
-    for (int e = 0; e < Vec16<T>::V; ++e) y[e] = x[at + e];
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, y), r, off, 0, POL);
+    for (int e = 0; e < VN; ++e) y[e] = x[at + e];
+    if constexpr (sizeof(VT) == 16)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, y), r, off, 0, POL);
+    else
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, y), r, off, 0, POL);
 }
 template <int POL>
 __device__ __forceinline__ void buf_store_elem(float x, __amdgpu_buffer_rsrc_t r, uint32_t off) {
@@ -200,21 +213,21 @@ struct MarchArgs {
     double fuse_limit;  // fused form allowed while sum |input| stays below this
 };
 
-// Strip geometry for KV 16-byte vectors per lane: K = KV*V columns per lane,
+// Strip geometry for KV lane vectors per lane: K = KV*V columns per lane,
 // 64*K per wave; the halo is TS columns rounded up to whole vectors.
-template <typename T, int KV> constexpr int march_k() { return KV * Vec16<T>::V; }
+template <typename T, int KV> constexpr int march_k(int ts) { return KV * lane_elems<T>(ts); }
 template <typename T, int KV> constexpr int march_halo(int ts) {
-    return ((ts + Vec16<T>::V - 1) / Vec16<T>::V) * Vec16<T>::V;
+    return ((ts + lane_elems<T>(ts) - 1) / lane_elems<T>(ts)) * lane_elems<T>(ts);
 }
 template <typename T, int KV> constexpr int march_out_width(int ts) {
-    return 64 * march_k<T, KV>() - 2 * march_halo<T, KV>(ts);
+    return 64 * march_k<T, KV>(ts) - 2 * march_halo<T, KV>(ts);
 }
 
 // One wave's march over output rows [row_out0, row_out1) and output columns
 // [col_out0, col_out0 + OW).  EDGE: some computed cell can lie on or outside
 // the grid boundary (first/last strip, first/last row tiles), so per-cell
 // row/column masks force those cells to 0; interior tiles skip every mask.
-// VEC: 16-byte aligned rows, KV 16-byte accesses per lane and row.
+// VEC: rows aligned to the lane vector, KV vector accesses per lane and row.
 // LPOL/SPOL: cache policy bits of the loads/stores (2 = non-temporal).
 // FUSED: cells use five_point_fused, and the lane adds up |x| over every value
 // it loads; the return value is true when that sum is not below `limit` (or is
@@ -224,8 +237,8 @@ template <typename T, int TS, int KV, bool VEC, bool EDGE, bool DOWN, int LPOL, 
 __device__ __forceinline__ bool march(const T *__restrict__ src, T *__restrict__ dst, int nx,
                                       int ny, int ld, T a, T limit, int lane, int col_out0,
                                       int row_out0, int row_out1) {
-    constexpr int V = Vec16<T>::V;
-    constexpr int K = march_k<T, KV>();
+    constexpr int V = lane_elems<T>(TS);
+    constexpr int K = march_k<T, KV>(TS);
     constexpr int HALO = march_halo<T, KV>(TS);
     constexpr int OW = march_out_width<T, KV>(TS);
     constexpr int ES = (int)sizeof(T);
@@ -286,7 +299,7 @@ __device__ __forceinline__ bool march(const T *__restrict__ src, T *__restrict__
         if (VEC) {
 #pragma unroll
             for (int v = 0; v < KV; ++v)
-                buf_load_vec<LPOL>(x, v * V, rin, roff + (uint32_t)(c0 + v * V) * ES);
+                buf_load_vec<LPOL, V>(x, v * V, rin, roff + (uint32_t)(c0 + v * V) * ES);
         } else {
 #pragma unroll
             for (int e = 0; e < K; ++e)
@@ -353,7 +366,7 @@ __device__ __forceinline__ bool march(const T *__restrict__ src, T *__restrict__
         const uint32_t qoff = (uint32_t)(r - DR * TS - row_out0) * row_bytes;
         if (VEC && !EDGE) {
 #pragma unroll
-            for (int v = 0; v < KV; ++v) buf_store_vec<SPOL>(out, v * V, rout, qoff + st_vec[v]);
+            for (int v = 0; v < KV; ++v) buf_store_vec<SPOL, V>(out, v * V, rout, qoff + st_vec[v]);
         } else {
 #pragma unroll
             for (int e = 0; e < K; ++e) buf_store_elem<SPOL>(out[e], rout, qoff + st_off[e]);
@@ -370,7 +383,7 @@ __device__ __forceinline__ bool march(const T *__restrict__ src, T *__restrict__
 
 template <typename T, int TS, int KV, bool VEC, int LPOL, int SPOL>
 __global__ __launch_bounds__(256) void k_march(MarchArgs g) {
-    constexpr int K = march_k<T, KV>();
+    constexpr int K = march_k<T, KV>(TS);
     constexpr int HALO = march_halo<T, KV>(TS);
     constexpr int OW = march_out_width<T, KV>(TS);
     static_assert(OW > 0, "time block too deep for the strip width");
@@ -500,7 +513,7 @@ __global__ __launch_bounds__(1024) void k_resident(const T *src, T *dst, T *prev
 // policies, and the tile height.
 constexpr int kLoadPolicy = 0;   // cache policy bits of the march's loads
 constexpr int kStorePolicy = 0;  // ... and of its stores
-// One 16-byte vector per lane: two (wider strips, half the halo) cost more
+// One lane vector per lane: two (wider strips, half the halo) cost more
 // registers than they save and measured slower at every depth.
 template <typename T> constexpr int vectors_per_lane(int) { return 1; }
 
@@ -612,9 +625,10 @@ int launch_march_kv(const void *src, void *dst, const DiffPlan &p, double alpha,
     const long row_bytes = (long)p.ld * (long)sizeof(T);
     const long max_rows = (1L << 30) / row_bytes - 2 * TS - 8;
     if (max_rows < 1) return fail(SGC_ERANGE, "grid rows too wide for the marching sweep");
-    const bool vec = (reinterpret_cast<uintptr_t>(src) % 16 == 0) &&
-                     (reinterpret_cast<uintptr_t>(dst) % 16 == 0) &&
-                     ((long)p.ld * (long)sizeof(T)) % 16 == 0;
+    constexpr uintptr_t VB = sizeof(T) * lane_elems<T>(TS);
+    const bool vec = (reinterpret_cast<uintptr_t>(src) % VB == 0) &&
+                     (reinterpret_cast<uintptr_t>(dst) % VB == 0) &&
+                     ((uintptr_t)p.ld * sizeof(T)) % VB == 0;
     auto kernel = vec ? k_march<T, TS, KV, true, kLoadPolicy, kStorePolicy>
                       : k_march<T, TS, KV, false, kLoadPolicy, kStorePolicy>;
     long rows = p.tile_rows;
