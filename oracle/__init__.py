@@ -63,6 +63,9 @@ def _load():
         lib.oracle_field_unpack.argtypes = [vp, i32, i64, i64, i64, i32, vp]
         lib.oracle_field_unpack.restype = ctypes.c_int
         lib.oracle_flux_diff.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i64, i64, vp]
+        lib.oracle_flux_stage.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, dbl, dbl, dbl, i32,
+                                          i64, i64, i64, vp]
+        lib.oracle_flux_stage.restype = ctypes.c_int
         lib.oracle_flux_diff.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -190,6 +193,37 @@ def flux_diff(fx, fy, fz, dx, dy, dz) -> np.ndarray:
                                   _ptr(dx), _ptr(dy), dz_p, nvar, nx, ny, nz, _ptr(rhs))
     assert rc == 0
     return rhs
+
+
+def flux_stage(fx, fy, fz, dx, dy, dz, q0, q, a: float, b: float, dt: float,
+               out: np.ndarray | None = None) -> np.ndarray:
+    """One SSPRK stage q' = a*q0 + b*(q + dt*rhs) on the flux difference rhs.
+
+    ``q0``, ``q`` (and ``out``) are (nvar, nz, ny, nx); ``out`` may be ``q``
+    or ``q0`` (updated in place).  Faces and spacings as for :func:`flux_diff`.
+    """
+    nvar, nz, ny, nxp1 = fx.shape
+    nx = nxp1 - 1
+    assert q0.shape == (nvar, nz, ny, nx) and q.shape == (nvar, nz, ny, nx)
+    fxl = [np.ascontiguousarray(fx[v]) for v in range(nvar)]
+    fyl = [np.ascontiguousarray(fy[v]) for v in range(nvar)]
+    fzl = [np.ascontiguousarray(fz[v]) for v in range(nvar)] if fz is not None else None
+    if out is None:
+        out = np.empty((nvar, nz, ny, nx), dtype=np.float64)
+    assert out.flags.c_contiguous and q0.flags.c_contiguous and q.flags.c_contiguous
+    dx = np.ascontiguousarray(dx, dtype=np.float64)
+    dy = np.ascontiguousarray(dy, dtype=np.float64)
+    if fz is not None:
+        dz = np.ascontiguousarray(dz, dtype=np.float64)
+        fz_tab, dz_p = _ptr_table(fzl), _ptr(dz)
+    else:
+        fz_tab, dz_p = None, None
+    rc = _load().oracle_flux_stage(_ptr_table(fxl), _ptr_table(fyl), fz_tab, _ptr(dx), _ptr(dy), dz_p,
+                                   _ptr_table([q0[v] for v in range(nvar)]),
+                                   _ptr_table([q[v] for v in range(nvar)]), float(a), float(b),
+                                   float(dt), nvar, nx, ny, nz, _ptr_table([out[v] for v in range(nvar)]))
+    assert rc == 0
+    return out
 
 
 # ---------------------------------------------------------------------------

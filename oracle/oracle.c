@@ -34,8 +34,17 @@
  *     contiguous;
  *   - the flux difference is rhs = (F_lo - F_hi) * (1/d) per direction, summed
  *     in the order x, y, z; cell j's low face is face j, its high face j+1.
+ *   [Mallard] Mallard documentation, "Design: single-GPU performance and
+ *         parallel scaling": Hardware and method (time steps are SSPRK3, three
+ *         stages) and the Baseline tables (per stage a right-hand side, a
+ *         division by the cell volume and an axpby update).  The pages give no
+ *         stage formula; the reading taken is the Shu-Osher form of SSPRK3,
+ *         q' = a*q0 + b*(q + dt*rhs) with (a, b) = (0, 1), (3/4, 1/4),
+ *         (1/3, 2/3), evaluated as t = dt*rhs; t = q + t; t = b*t; s = a*q0;
+ *         q' = s + t, one rounding each.
  */
 #include <stddef.h>
+#include <stdlib.h>
 #include <stdint.h>
 
 /* ------------------------------------------------------------------------ */
@@ -240,5 +249,42 @@ int oracle_flux_diff(const double *const *fx, const double *const *fy,
                     rhs[j + nx * (k + ny * (l + nz * (int64_t)var))] = r;
                 }
     }
+    return 0;
+}
+
+/*
+ * One SSPRK stage on the flux difference ([Mallard] Hardware and method,
+ * Baseline): per cell and variable, r is the flux difference of
+ * oracle_flux_diff, then qout = a*q0 + b*(q + dt*r) in the order
+ * t = dt*r; t = q + t; t = b*t; s = a*q0; qout = s + t.  q0, q and qout are
+ * tables of nvar fields of nx*ny*nz doubles (j fastest).  qout may be q or q0
+ * (each cell is read before it is written).  Returns 0, or 1 for a 2D call
+ * with nz != 1, 2 if the scratch rhs cannot be allocated.
+ */
+int oracle_flux_stage(const double *const *fx, const double *const *fy,
+                      const double *const *fz, const double *dx,
+                      const double *dy, const double *dz,
+                      const double *const *q0, const double *const *q,
+                      double a, double b, double dt, int32_t nvar,
+                      int64_t nx, int64_t ny, int64_t nz, double *const *qout)
+{
+    const int64_t n = nx * ny * nz;
+    double *rhs = (double *)malloc((size_t)(n * nvar) * sizeof(double));
+    if (rhs == NULL)
+        return 2;
+    const int rc = oracle_flux_diff(fx, fy, fz, dx, dy, dz, nvar, nx, ny, nz, rhs);
+    if (rc != 0) {
+        free(rhs);
+        return rc;
+    }
+    for (int32_t var = 0; var < nvar; ++var)
+        for (int64_t c = 0; c < n; ++c) {
+            double t = dt * rhs[c + n * var];
+            t = q[var][c] + t;
+            t = b * t;
+            const double s = a * q0[var][c];
+            qout[var][c] = s + t;
+        }
+    free(rhs);
     return 0;
 }

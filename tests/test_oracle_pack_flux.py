@@ -184,3 +184,71 @@ def test_two_d_form_equals_three_d_with_zero_z():
     a = oracle.flux_diff(fi.fx, fi.fy, None, fi.dx, fi.dy, None)
     b = oracle.flux_diff(fi.fx, fi.fy, fz, fi.dx, fi.dy, dz)
     assert np.array_equal(a, b)
+
+
+# ---------------------------------------------------------------------------
+# SSPRK stage fused with the flux difference
+# (Mallard documentation, "Design: single-GPU performance and parallel
+# scaling": Hardware and method -- time steps are SSPRK3, three stages -- and
+# the Baseline tables -- per stage a right-hand side and an axpby update.  The
+# stage form q' = a*q0 + b*(q + dt*rhs) with (a, b) = (0, 1), (3/4, 1/4),
+# (1/3, 2/3) is the Shu-Osher reading of SSPRK3.)
+# ---------------------------------------------------------------------------
+
+SSPRK3 = [(0.0, 1.0), (0.75, 0.25), (1.0 / 3.0, 2.0 / 3.0)]
+
+
+def _stage_inputs(nvar, nx, ny, nz, seed, two_d=False):
+    fi = inputs.normal_faces(nvar, nx, ny, nz, seed, two_d=two_d)
+    g = np.random.Generator(np.random.PCG64(seed + 1))
+    q0 = g.standard_normal((nvar, nz, ny, nx))
+    return fi, q0
+
+
+@pytest.mark.parametrize("two_d", [False, True])
+def test_ssprk3_step_with_fixed_fluxes_is_one_euler_step(two_d):
+    """With face fluxes that do not depend on q, the three Shu-Osher stages
+    collapse to q3 = q0 + dt*rhs (q1 = q0 + dt*r, q2 = q0 + dt*r/2,
+    q3 = q0 + dt*r): a closed form that a wrong coefficient, sign, or dt
+    placement breaks by O(dt*|rhs|).  Tolerance: a few roundings of |q|."""
+    nz = 1 if two_d else 5
+    fi, q0 = _stage_inputs(3, 7, 6, nz, 801, two_d)
+    fz, dz = (None, None) if two_d else (fi.fz, fi.dz)
+    dt = 0.01
+    q = q0
+    for a, b in SSPRK3:
+        q = oracle.flux_stage(fi.fx, fi.fy, fz, fi.dx, fi.dy, dz, q0, q, a, b, dt)
+    rhs = oracle.flux_diff(fi.fx, fi.fy, fz, fi.dx, fi.dy, dz)
+    expect = q0 + dt * rhs
+    scale = np.abs(q0).max() + dt * np.abs(rhs).max()
+    assert np.abs(q - expect).max() <= 16 * np.finfo(np.float64).eps * scale
+    # and the stages are not the identity: dt*rhs is far above that tolerance
+    assert np.abs(dt * rhs).max() > 1e6 * np.finfo(np.float64).eps * scale
+
+
+def test_constant_fluxes_give_the_axpby_exactly():
+    """Constant faces make rhs exactly 0, so the stage is a*q0 + b*q; with
+    dyadic a, b and small-integer states every operation is exact."""
+    nvar, nx, ny, nz = 2, 5, 4, 3
+    fx = np.full((nvar, nz, ny, nx + 1), 3.0)
+    fy = np.full((nvar, nz, ny + 1, nx), -2.0)
+    fz = np.full((nvar, nz + 1, ny, nx), 7.0)
+    d = np.full(8, 0.3)
+    g = np.random.Generator(np.random.PCG64(802))
+    q0 = g.integers(-50, 50, (nvar, nz, ny, nx)).astype(np.float64)
+    q = g.integers(-50, 50, (nvar, nz, ny, nx)).astype(np.float64)
+    out = oracle.flux_stage(fx, fy, fz, d[:nx], d[:ny], d[:nz], q0, q, 0.75, 0.25, 0.125)
+    expect = np.array([[[[Fraction(3, 4) * Fraction(int(x0)) + Fraction(1, 4) * Fraction(int(x))
+                          for x0, x in zip(r0, r)] for r0, r in zip(p0, p)] for p0, p in zip(v0, v)]
+                       for v0, v in zip(q0, q)], dtype=object)
+    assert np.array_equal(out, expect.astype(np.float64))
+    assert all(float(e) == float(Fraction(e)) for e in expect.reshape(-1))
+
+
+def test_stage_in_place_equals_out_of_place():
+    fi, q0 = _stage_inputs(2, 6, 5, 4, 803)
+    q = q0 * 0.5 + 1.0
+    ref = oracle.flux_stage(fi.fx, fi.fy, fi.fz, fi.dx, fi.dy, fi.dz, q0, q, 0.75, 0.25, 0.02)
+    qq = q.copy()
+    oracle.flux_stage(fi.fx, fi.fy, fi.fz, fi.dx, fi.dy, fi.dz, q0, qq, 0.75, 0.25, 0.02, out=qq)
+    assert np.array_equal(qq, ref)
