@@ -20,7 +20,8 @@ Prints ONE JSON line with:
   cpu_baseline  the CPU oracle (single thread) on a bounded sample of the
               same workload, timed on this host;
   kernels     per-kernel figures for the other workloads (pack along x/y/z,
-              flux difference, the 2D workload, the page's three loop layouts,
+              flux difference and its fused SSPRK stage, the 2D workload, the
+              page's three loop layouts, the resident small-grid map,
               FP32, a 16-byte copy for reference), each as time, cell-var
               updates/s and GB/s of minimal traffic with the MALL flushed
               before every single-pass repetition.
@@ -375,7 +376,18 @@ def measure_all(log) -> dict:
         t = timed(lambda: binding.flux_diff3d(*args, rhs=rhs, map=m), 5, True)
         res[f"flux_201x101x101_x7_{m}"] = entry(t, cv, nbytes)
         log("flux", m, res[f"flux_201x101x101_x7_{m}"])
-    del args, rhs
+    # one SSPRK stage fused with it: reads q0 and q, writes q' instead of rhs
+    q0 = dev(inputs.normal_fields(nvar, nxc, nyc, nzc, 1060))
+    qs = dev(inputs.normal_fields(nvar, nxc, nyc, nzc, 1061))
+    qo = torch.empty_like(qs)
+    sbytes = nbytes + 2 * 8 * cv
+    for m in ("tiled", "per_cell", "per_cellvar"):
+        binding.flux_stage3d(*args, q0, qs, 0.75, 0.25, 1e-3, out=qo, map=m)
+        t = timed(lambda: binding.flux_stage3d(*args, q0, qs, 0.75, 0.25, 1e-3, out=qo, map=m), 5, True)
+        res[f"flux_stage_201x101x101_x7_{m}"] = entry(
+            t, cv, sbytes, {"note": "a separate update pass would add one write and one read of rhs"})
+        log("flux stage", m, res[f"flux_stage_201x101x101_x7_{m}"])
+    del args, rhs, q0, qs, qo
     torch.cuda.empty_cache()
 
     # 2D workload, 6 x 4800x1200: flux difference and packs along x, y
@@ -390,7 +402,15 @@ def measure_all(log) -> dict:
         t = timed(lambda: binding.flux_diff3d(*args, rhs=rhs, map=m), 5, True)
         res[f"flux2d_4800x1200_x6_{m}"] = entry(t, cv, nbytes)
         log("flux2d", m, res[f"flux2d_4800x1200_x6_{m}"])
-    del args, rhs
+    q0 = dev(inputs.normal_fields(nvar, nxc, nyc, 1, 1062))
+    qs = dev(inputs.normal_fields(nvar, nxc, nyc, 1, 1063))
+    qo = torch.empty_like(qs)
+    sbytes = nbytes + 2 * 8 * cv
+    binding.flux_stage3d(*args, q0, qs, 0.75, 0.25, 1e-3, out=qo)
+    t = timed(lambda: binding.flux_stage3d(*args, q0, qs, 0.75, 0.25, 1e-3, out=qo), 5, True)
+    res["flux_stage2d_4800x1200_x6_tiled"] = entry(t, cv, sbytes)
+    log("flux2d stage", res["flux_stage2d_4800x1200_x6_tiled"])
+    del args, rhs, q0, qs, qo
     f = dev(inputs.cfg5_fields())
     out = torch.empty(cv, dtype=torch.float64, device="cuda")
     for d, dn in ((0, "x"), (1, "y")):

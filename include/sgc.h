@@ -199,6 +199,35 @@ SGC_API int flux_diff3d(const double *const *fx, const double *const *fy,
                 const double *dz, int32_t nvar, int64_t nx, int64_t ny,
                 int64_t nz, double *rhs, int32_t map, void *stream);
 
+/*
+ * flux_stage3d -- one SSPRK stage fused with the flux difference (Mallard
+ * documentation, "Design: single-GPU performance and parallel scaling":
+ * Hardware and method -- time steps are SSPRK3, three stages -- and the
+ * Baseline tables, where each stage computes a right-hand side and applies
+ * an axpby update).  The pages give no stage formula; this is the Shu-Osher
+ * form, per cell and variable
+ *   q'(j,k,l,v) = a*q0 + b*(q + dt*rhs)
+ * with rhs exactly as flux_diff3d computes it, evaluated t = dt*rhs;
+ * t = q + t; t = b*t; s = a*q0; q' = s + t (one rounding each).  SSPRK3 uses
+ * (a, b) = (0, 1), (3/4, 1/4), (1/3, 2/3).  rhs is never stored.
+ *
+ *   fx .. dz, nvar, nx, ny, nz   as flux_diff3d.
+ *   q0, q       HOST arrays of nvar DEVICE pointers, each field nx*ny*nz
+ *               doubles, j fastest (the stage's base state and its input).
+ *   a, b, dt    finite.
+ *   qout        HOST array of nvar DEVICE pointers, written.  qout[v] may be
+ *               the same pointer as q[v] or q0[v] (updated in place); it must
+ *               not otherwise overlap any input or another output.
+ *   map         an sgc_var_map.
+ * Every map returns identical bits.  Errors as flux_diff3d (SGC_EALIAS for a
+ * disallowed overlap), all before anything is enqueued.
+ */
+SGC_API int flux_stage3d(const double *const *fx, const double *const *fy,
+                         const double *const *fz, const double *dx, const double *dy,
+                         const double *dz, const double *const *q0, const double *const *q,
+                         double a, double b, double dt, int32_t nvar, int64_t nx, int64_t ny,
+                         int64_t nz, double *const *qout, int32_t map, void *stream);
+
 /* Message for the last non-OK return on the calling thread ("" if none). */
 SGC_API const char *sgc_last_error(void);
 

@@ -66,6 +66,9 @@ def load() -> ctypes.CDLL:
     lib.field_unpack.restype = ctypes.c_int
     lib.flux_diff3d.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i64, i64, vp, i32, vp]
     lib.flux_diff3d.restype = ctypes.c_int
+    lib.flux_stage3d.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, dbl, dbl, dbl, i32, i64, i64, i64,
+                                 vp, i32, vp]
+    lib.flux_stage3d.restype = ctypes.c_int
     lib.sgc_last_error.argtypes = []
     lib.sgc_last_error.restype = ctypes.c_char_p
     lib.sgc_abi_version.argtypes = []
@@ -228,3 +231,36 @@ def flux_diff3d(fx, fy, fz, dx: torch.Tensor, dy: torch.Tensor, dz: torch.Tensor
                             nvar, nx, ny, nz, _dev_ptr(rhs), m, _stream_ptr(stream))
     _check(rc)
     return rhs
+
+
+def flux_stage3d(fx, fy, fz, dx: torch.Tensor, dy: torch.Tensor, dz: torch.Tensor | None,
+                 q0, q, a: float, b: float, dt: float, out=None, map: str | int = "tiled",
+                 stream=None):
+    """One SSPRK stage q' = a*q0 + b*(q + dt*rhs) fused with the flux difference.
+
+    q0, q and out are nvar fields of (nz, ny, nx) float64 (a stacked tensor or
+    a list); out defaults to a new (nvar, nz, ny, nx) tensor and may be q or
+    q0 (updated in place).  Faces and spacings as for :func:`flux_diff3d`.
+    """
+    fxl, fyl = _as_list(fx), _as_list(fy)
+    fzl = _as_list(fz) if fz is not None else None
+    nvar = len(fxl)
+    nz, ny, nxp1 = fxl[0].shape
+    nx = nxp1 - 1
+    q0l, ql = _as_list(q0), _as_list(q)
+    if out is None:
+        out = torch.empty((nvar, nz, ny, nx), dtype=torch.float64, device=fxl[0].device)
+    outl = _as_list(out)
+    for name, lst in (("q0", q0l), ("q", ql), ("out", outl)):
+        if len(lst) != nvar:
+            raise ValueError(f"{name} must hold {nvar} fields")
+        for t in lst:
+            if t.dtype != torch.float64 or tuple(t.shape) != (nz, ny, nx):
+                raise ValueError(f"{name} fields must be float64 (nz, ny, nx)")
+    m = VAR_MAPS[map] if isinstance(map, str) else int(map)
+    rc = load().flux_stage3d(_table(fxl), _table(fyl), _table(fzl) if fzl is not None else None,
+                             _dev_ptr(dx), _dev_ptr(dy), _dev_ptr(dz) if dz is not None else None,
+                             _table(q0l), _table(ql), float(a), float(b), float(dt), nvar, nx, ny, nz,
+                             _table(outl), m, _stream_ptr(stream))
+    _check(rc)
+    return out

@@ -91,6 +91,54 @@ int check_ptr(const char *fn, const char *name, const double *p) {
     return SGC_OK;
 }
 
+// Faces, spacings and extents of a flux call (the 2D form has fz == dz == NULL
+// and nz == 1).
+int check_flux_inputs(const char *fn, const double *const *fx, const double *const *fy,
+                      const double *const *fz, const double *dx, const double *dy, const double *dz,
+                      int32_t nvar, int64_t nx, int64_t ny, int64_t nz) {
+    int rc;
+    if ((rc = check_dims(fn, nvar, nx, ny, nz))) return rc;
+    if ((rc = check_table(fn, "fx", fx, nvar))) return rc;
+    if ((rc = check_table(fn, "fy", fy, nvar))) return rc;
+    if (fz != nullptr && (rc = check_table(fn, "fz", fz, nvar))) return rc;
+    if ((rc = check_ptr(fn, "dx", dx))) return rc;
+    if ((rc = check_ptr(fn, "dy", dy))) return rc;
+    if ((fz == nullptr) != (dz == nullptr))
+        return fail(SGC_ENULL, std::string(fn) + ": fz and dz must both be given or both be NULL");
+    if (dz != nullptr && (rc = check_ptr(fn, "dz", dz))) return rc;
+    if (fz == nullptr && nz != 1) return fail(SGC_EINVAL, std::string(fn) + ": the 2D form (fz NULL) needs nz == 1");
+    if ((nx + 1) * (ny + 1) > kMaxElems / (nz + 1) || nx * ny * nz > kMaxElems / nvar)
+        return fail(SGC_ERANGE, std::string(fn) + ": an array exceeds 2^31-1 elements");
+    return SGC_OK;
+}
+
+// An output region must not overlap any face or spacing array.
+int check_output_vs_flux_inputs(const char *fn, const char *name, const void *out, int64_t obytes,
+                                const double *const *fx, const double *const *fy, const double *const *fz,
+                                const double *dx, const double *dy, const double *dz, int32_t nvar,
+                                int64_t nx, int64_t ny, int64_t nz) {
+    const int64_t nfx = (nx + 1) * ny * nz, nfy = nx * (ny + 1) * nz, nfz = nx * ny * (nz + 1);
+    for (int32_t k = 0; k < nvar; ++k) {
+        if (overlaps(out, obytes, fx[k], nfx * 8)) return fail(SGC_EALIAS, std::string(fn) + ": " + name + " overlaps fx");
+        if (overlaps(out, obytes, fy[k], nfy * 8)) return fail(SGC_EALIAS, std::string(fn) + ": " + name + " overlaps fy");
+        if (fz && overlaps(out, obytes, fz[k], nfz * 8))
+            return fail(SGC_EALIAS, std::string(fn) + ": " + name + " overlaps fz");
+    }
+    if (overlaps(out, obytes, dx, nx * 8) || overlaps(out, obytes, dy, ny * 8) ||
+        (dz && overlaps(out, obytes, dz, nz * 8)))
+        return fail(SGC_EALIAS, std::string(fn) + ": " + name + " overlaps a spacing array");
+    return SGC_OK;
+}
+
+void flux_tables(const double *const *fx, const double *const *fy, const double *const *fz, int32_t nvar,
+                 PtrTable &tx, PtrTable &ty, PtrTable &tz) {
+    for (int32_t k = 0; k < nvar; ++k) {
+        tx.p[k] = fx[k];
+        ty.p[k] = fy[k];
+        if (fz) tz.p[k] = fz[k];
+    }
+}
+
 }  // namespace
 
 extern "C" {
@@ -238,39 +286,61 @@ int flux_diff3d(const double *const *fx, const double *const *fy, const double *
                 int64_t ny, int64_t nz, double *rhs, int32_t map, void *stream) {
     clear();
     int rc;
-    if ((rc = check_dims("flux_diff3d", nvar, nx, ny, nz))) return rc;
-    if ((rc = check_table("flux_diff3d", "fx", fx, nvar))) return rc;
-    if ((rc = check_table("flux_diff3d", "fy", fy, nvar))) return rc;
-    if (fz != nullptr && (rc = check_table("flux_diff3d", "fz", fz, nvar))) return rc;
-    if ((rc = check_ptr("flux_diff3d", "dx", dx))) return rc;
-    if ((rc = check_ptr("flux_diff3d", "dy", dy))) return rc;
-    if ((fz == nullptr) != (dz == nullptr))
-        return fail(SGC_ENULL, "flux_diff3d: fz and dz must both be given or both be NULL");
-    if (dz != nullptr && (rc = check_ptr("flux_diff3d", "dz", dz))) return rc;
-    if (fz == nullptr && nz != 1) return fail(SGC_EINVAL, "flux_diff3d: the 2D form (fz NULL) needs nz == 1");
+    if ((rc = check_flux_inputs("flux_diff3d", fx, fy, fz, dx, dy, dz, nvar, nx, ny, nz))) return rc;
     if ((rc = check_ptr("flux_diff3d", "rhs", rhs))) return rc;
     if (map < SGC_VAR_PER_CELL || map > SGC_VAR_TILED) return fail(SGC_EINVAL, "flux_diff3d: unknown map");
-    const int64_t nfx = (nx + 1) * ny * nz, nfy = nx * (ny + 1) * nz, nfz = nx * ny * (nz + 1);
     const int64_t n = nx * ny * nz;
-    if ((nx + 1) * (ny + 1) > kMaxElems / (nz + 1) || n > kMaxElems / nvar)
-        return fail(SGC_ERANGE, "flux_diff3d: an array exceeds 2^31-1 elements");
-    const int64_t rbytes = n * nvar * 8;
-    for (int32_t k = 0; k < nvar; ++k) {
-        if (overlaps(rhs, rbytes, fx[k], nfx * 8)) return fail(SGC_EALIAS, "flux_diff3d: rhs overlaps fx");
-        if (overlaps(rhs, rbytes, fy[k], nfy * 8)) return fail(SGC_EALIAS, "flux_diff3d: rhs overlaps fy");
-        if (fz && overlaps(rhs, rbytes, fz[k], nfz * 8)) return fail(SGC_EALIAS, "flux_diff3d: rhs overlaps fz");
-    }
-    if (overlaps(rhs, rbytes, dx, nx * 8) || overlaps(rhs, rbytes, dy, ny * 8) ||
-        (dz && overlaps(rhs, rbytes, dz, nz * 8)))
-        return fail(SGC_EALIAS, "flux_diff3d: rhs overlaps a spacing array");
+    if ((rc = check_output_vs_flux_inputs("flux_diff3d", "rhs", rhs, n * nvar * 8, fx, fy, fz, dx, dy, dz,
+                                          nvar, nx, ny, nz)))
+        return rc;
     PtrTable tx{}, ty{}, tz{};
+    flux_tables(fx, fy, fz, nvar, tx, ty, tz);
+    return flux_launch(tx, ty, fz ? &tz : nullptr, dx, dy, dz, nvar, (int)nx, (int)ny, (int)nz, rhs,
+                       nullptr, map, static_cast<hipStream_t>(stream));
+}
+
+int flux_stage3d(const double *const *fx, const double *const *fy, const double *const *fz,
+                 const double *dx, const double *dy, const double *dz, const double *const *q0,
+                 const double *const *q, double a, double b, double dt, int32_t nvar, int64_t nx,
+                 int64_t ny, int64_t nz, double *const *qout, int32_t map, void *stream) {
+    clear();
+    int rc;
+    if ((rc = check_flux_inputs("flux_stage3d", fx, fy, fz, dx, dy, dz, nvar, nx, ny, nz))) return rc;
+    if ((rc = check_table("flux_stage3d", "q0", q0, nvar))) return rc;
+    if ((rc = check_table("flux_stage3d", "q", q, nvar))) return rc;
+    if ((rc = check_table("flux_stage3d", "qout", qout, nvar))) return rc;
+    if (!std::isfinite(a) || !std::isfinite(b) || !std::isfinite(dt))
+        return fail(SGC_EINVAL, "flux_stage3d: a, b and dt must be finite");
+    if (map < SGC_VAR_PER_CELL || map > SGC_VAR_TILED) return fail(SGC_EINVAL, "flux_stage3d: unknown map");
+    const int64_t fb = nx * ny * nz * 8;  // bytes per field
     for (int32_t k = 0; k < nvar; ++k) {
-        tx.p[k] = fx[k];
-        ty.p[k] = fy[k];
-        if (fz) tz.p[k] = fz[k];
+        if ((rc = check_output_vs_flux_inputs("flux_stage3d", "qout", qout[k], fb, fx, fy, fz, dx, dy, dz,
+                                              nvar, nx, ny, nz)))
+            return rc;
+        for (int32_t m = 0; m < nvar; ++m) {
+            if (m != k && overlaps(qout[k], fb, qout[m], fb))
+                return fail(SGC_EALIAS, "flux_stage3d: two qout fields overlap");
+            // q' may replace q or q0 of its own variable in place, nothing else
+            const bool same_var = m == k;
+            if (overlaps(qout[k], fb, q[m], fb) && !(same_var && qout[k] == q[m]))
+                return fail(SGC_EALIAS, "flux_stage3d: qout overlaps a q field other than its own");
+            if (overlaps(qout[k], fb, q0[m], fb) && !(same_var && qout[k] == q0[m]))
+                return fail(SGC_EALIAS, "flux_stage3d: qout overlaps a q0 field other than its own");
+        }
     }
-    return flux_launch(tx, ty, fz ? &tz : nullptr, dx, dy, dz, nvar, (int)nx, (int)ny, (int)nz, rhs, map,
-                       static_cast<hipStream_t>(stream));
+    PtrTable tx{}, ty{}, tz{};
+    flux_tables(fx, fy, fz, nvar, tx, ty, tz);
+    StageArgs st{};
+    for (int32_t k = 0; k < nvar; ++k) {
+        st.q0.p[k] = q0[k];
+        st.q.p[k] = q[k];
+        st.qout.p[k] = qout[k];
+    }
+    st.a = a;
+    st.b = b;
+    st.dt = dt;
+    return flux_launch(tx, ty, fz ? &tz : nullptr, dx, dy, dz, nvar, (int)nx, (int)ny, (int)nz, nullptr,
+                       &st, map, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -20,6 +20,15 @@
 //     the five arrays of about one variable: streaming many arrays at once
 //     (all variables per thread) measured 10-13% slower on MI355X.  The 2D
 //     form marches along k instead, treating Fy as the marched face.
+//
+// Stage variant (flux_stage3d): the same right-hand side r feeds one SSPRK
+// stage in the same thread, q' = a*q0 + b*(q + dt*r) (Mallard documentation,
+// "Design: single-GPU performance and parallel scaling": SSPRK3 time steps
+// with a right-hand side and an axpby update per stage; the Shu-Osher stage
+// form is this library's reading), evaluated t = dt*r; t = q + t; t = b*t;
+// s = a*q0; q' = s + t with one rounding each.  r never goes to memory: per
+// cell and variable the fused pass reads q0 and q and writes q' instead of
+// writing r and re-reading it for a separate update.
 #include "sgc_internal.h"
 
 namespace sgc {
@@ -30,6 +39,7 @@ struct FluxArgs {
     const double *dx, *dy, *dz;
     double *rhs;
     int nvar, nx, ny, nz;
+    StageArgs st;  // stage variant only
 };
 
 __device__ __forceinline__ double face_term(double lo, double hi, double inv) {
@@ -42,8 +52,32 @@ __device__ __forceinline__ double add(double a, double b) {
     return a + b;
 }
 
+// q' = a*q0 + b*(q + dt*r), one rounding per operation in this order.
+__device__ __forceinline__ double stage(double r, double q0, double q, const StageArgs &st) {
+#pragma clang fp contract(off)
+    double t = st.dt * r;
+    t = q + t;
+    t = st.b * t;
+    const double s = st.a * q0;
+    return s + t;
+}
+
+// Output of variable v at flat cell index cell (j + nx*(k + ny*l)): the rhs
+// entry, or the stage update of the state.  The state pointers may alias each
+// other (q' in place of q or q0); each cell is read before it is written, by
+// the same thread.
+template <bool STAGE>
+__device__ __forceinline__ void put(const FluxArgs &g, int v, long n, long cell, double r) {
+    if (STAGE) {
+        double *out = const_cast<double *>(g.st.qout.p[v]);
+        out[cell] = stage(r, g.st.q0.p[v][cell], g.st.q.p[v][cell], g.st);
+    } else {
+        g.rhs[cell + (long)v * n] = r;
+    }
+}
+
 // One thread per cell; variables looped inside the thread.
-template <bool HAS_Z>
+template <bool HAS_Z, bool STAGE>
 __global__ __launch_bounds__(256) void k_flux_per_cell(FluxArgs g) {
     const int n = g.nx * g.ny * g.nz;
     const int idx = blockIdx.x * 256 + threadIdx.x;
@@ -62,12 +96,12 @@ __global__ __launch_bounds__(256) void k_flux_per_cell(FluxArgs g) {
         double r = face_term(g.fx.p[v][ox], g.fx.p[v][ox + 1], ix);
         r = add(r, face_term(g.fy.p[v][oy], g.fy.p[v][oy + g.nx], iy));
         if (HAS_Z) r = add(r, face_term(g.fz.p[v][idx], g.fz.p[v][idx + sz], iz));
-        g.rhs[idx + v * n] = r;
+        put<STAGE>(g, v, n, idx, r);
     }
 }
 
 // One thread per (var, cell): everything recomputed per thread.
-template <bool HAS_Z>
+template <bool HAS_Z, bool STAGE>
 __global__ __launch_bounds__(256) void k_flux_per_cellvar(FluxArgs g) {
     const int n = g.nx * g.ny * g.nz;
     const int idx = blockIdx.x * 256 + threadIdx.x;
@@ -89,7 +123,7 @@ __global__ __launch_bounds__(256) void k_flux_per_cellvar(FluxArgs g) {
         const double iz = 1.0 / g.dz[l];
         r = add(r, face_term(g.fz.p[v][oc], g.fz.p[v][oc + g.nx * g.ny], iz));
     }
-    g.rhs[oc + v * n] = r;
+    put<STAGE>(g, v, n, oc, r);
 }
 
 // Column pencils marching the slowest axis.  View (nxv, nyv, nzv): the 3D
@@ -108,7 +142,7 @@ struct PencilArgs {
 };
 
 
-template <bool HAS_Y>
+template <bool HAS_Y, bool STAGE>
 __global__ __launch_bounds__(256) void k_flux_pencil(PencilArgs a) {
     __shared__ double iz_s[kMaxPlanes];
     const FluxArgs &g = a.g;
@@ -141,7 +175,7 @@ __global__ __launch_bounds__(256) void k_flux_pencil(PencilArgs a) {
     const double *__restrict__ FX = g.fx.p[v];
     const double *__restrict__ FY = g.fy.p[v];
     const double *__restrict__ FZ = HAS_Y ? g.fz.p[v] : g.fy.p[v];
-    double *__restrict__ R = g.rhs + (long)v * n;
+
     double zlo = FZ[c + sc * l0];
     for (int l = l0; l < l1; ++l) {
         const double xl = FX[ox + sx * l];
@@ -155,7 +189,7 @@ __global__ __launch_bounds__(256) void k_flux_pencil(PencilArgs a) {
         double r = face_term(xl, xh, ix);
         if (HAS_Y) r = add(r, face_term(yl, yh, iy));
         r = add(r, face_term(zlo, zh, iz_s[l - l0]));
-        R[c + sc * l] = r;
+        put<STAGE>(g, v, n, c + (long)sc * l, r);
         zlo = zh;
     }
 }
@@ -166,11 +200,52 @@ __global__ __launch_bounds__(256) void k_flux_pencil(PencilArgs a) {
 // run boundary are the only ones read twice.
 constexpr int kTargetWaves = 262144;
 
+template <bool STAGE>
+int flux_launch_t(const FluxArgs &g, bool has_z, int map, hipStream_t s) {
+    const long n = (long)g.nx * g.ny * g.nz;
+    if (map == SGC_VAR_PER_CELL) {
+        const dim3 grid((unsigned)((n + 255) / 256));
+        if (has_z) hipLaunchKernelGGL((k_flux_per_cell<true, STAGE>), grid, dim3(256), 0, s, g);
+        else hipLaunchKernelGGL((k_flux_per_cell<false, STAGE>), grid, dim3(256), 0, s, g);
+        return check_launch("flux difference, one thread per cell");
+    }
+    if (map == SGC_VAR_PER_CELLVAR) {
+        const dim3 grid((unsigned)((n * g.nvar + 255) / 256));
+        if (has_z) hipLaunchKernelGGL((k_flux_per_cellvar<true, STAGE>), grid, dim3(256), 0, s, g);
+        else hipLaunchKernelGGL((k_flux_per_cellvar<false, STAGE>), grid, dim3(256), 0, s, g);
+        return check_launch("flux difference, one thread per (var, cell)");
+    }
+    if (map != SGC_VAR_TILED) return fail(SGC_EINVAL, "unknown variable map");
+    PencilArgs a;
+    a.g = g;
+    if (has_z) {
+        a.nxv = g.nx; a.nyv = g.ny; a.nzv = g.nz;
+    } else {
+        a.nxv = g.nx; a.nyv = 1; a.nzv = g.ny;
+    }
+    const long ncols = (long)a.nxv * a.nyv;
+    a.col_blocks = (int)((ncols + 255) / 256);
+    const long waves_per_run = (ncols + 63) / 64;
+    long runs = (kTargetWaves + waves_per_run * g.nvar - 1) / (waves_per_run * g.nvar);
+    if (runs < 1) runs = 1;
+    int planes = (int)((a.nzv + runs - 1) / runs);
+    planes = planes < 2 ? 2 : planes;
+    planes = planes > kMaxPlanes ? kMaxPlanes : planes;
+    planes = planes > a.nzv ? a.nzv : planes;
+    a.planes = planes;
+    a.runs = (a.nzv + planes - 1) / planes;
+    a.per_var = ((a.col_blocks * a.runs + 7) / 8) * 8;
+    const long blocks = (long)a.per_var * g.nvar;
+    if (has_z) hipLaunchKernelGGL((k_flux_pencil<true, STAGE>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_flux_pencil<false, STAGE>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+    return check_launch("flux difference, column pencils");
+}
+
 }  // namespace
 
 int flux_launch(const PtrTable &fx, const PtrTable &fy, const PtrTable *fz, const double *dx,
-                const double *dy, const double *dz, int nvar, int nx, int ny, int nz, double *rhs, int map,
-                hipStream_t s) {
+                const double *dy, const double *dz, int nvar, int nx, int ny, int nz, double *rhs,
+                const StageArgs *st, int map, hipStream_t s) {
     FluxArgs g{};
     g.fx = fx;
     g.fy = fy;
@@ -183,44 +258,9 @@ int flux_launch(const PtrTable &fx, const PtrTable &fy, const PtrTable *fz, cons
     g.nx = nx;
     g.ny = ny;
     g.nz = nz;
+    if (st) g.st = *st;
     const bool has_z = fz != nullptr;
-    const long n = (long)nx * ny * nz;
-    if (map == SGC_VAR_PER_CELL) {
-        const dim3 grid((unsigned)((n + 255) / 256));
-        if (has_z) hipLaunchKernelGGL((k_flux_per_cell<true>), grid, dim3(256), 0, s, g);
-        else hipLaunchKernelGGL((k_flux_per_cell<false>), grid, dim3(256), 0, s, g);
-        return check_launch("flux difference, one thread per cell");
-    }
-    if (map == SGC_VAR_PER_CELLVAR) {
-        const dim3 grid((unsigned)((n * nvar + 255) / 256));
-        if (has_z) hipLaunchKernelGGL((k_flux_per_cellvar<true>), grid, dim3(256), 0, s, g);
-        else hipLaunchKernelGGL((k_flux_per_cellvar<false>), grid, dim3(256), 0, s, g);
-        return check_launch("flux difference, one thread per (var, cell)");
-    }
-    if (map != SGC_VAR_TILED) return fail(SGC_EINVAL, "unknown variable map");
-    PencilArgs a;
-    a.g = g;
-    if (has_z) {
-        a.nxv = nx; a.nyv = ny; a.nzv = nz;
-    } else {
-        a.nxv = nx; a.nyv = 1; a.nzv = ny;
-    }
-    const long ncols = (long)a.nxv * a.nyv;
-    a.col_blocks = (int)((ncols + 255) / 256);
-    const long waves_per_run = (ncols + 63) / 64;
-    long runs = (kTargetWaves + waves_per_run * nvar - 1) / (waves_per_run * nvar);
-    if (runs < 1) runs = 1;
-    int planes = (int)((a.nzv + runs - 1) / runs);
-    planes = planes < 2 ? 2 : planes;
-    planes = planes > kMaxPlanes ? kMaxPlanes : planes;
-    planes = planes > a.nzv ? a.nzv : planes;
-    a.planes = planes;
-    a.runs = (a.nzv + planes - 1) / planes;
-    a.per_var = ((a.col_blocks * a.runs + 7) / 8) * 8;
-    const long blocks = (long)a.per_var * nvar;
-    if (has_z) hipLaunchKernelGGL((k_flux_pencil<true>), dim3((unsigned)blocks), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((k_flux_pencil<false>), dim3((unsigned)blocks), dim3(256), 0, s, a);
-    return check_launch("flux difference, column pencils");
+    return st ? flux_launch_t<true>(g, has_z, map, s) : flux_launch_t<false>(g, has_z, map, s);
 }
 
 }  // namespace sgc

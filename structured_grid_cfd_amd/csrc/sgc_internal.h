@@ -74,8 +74,15 @@ int pack_launch(const PtrTable &fields, int nvar, int nx, int ny, int nz, int di
                 double *out, int map, hipStream_t s);
 int unpack_launch(const double *packed, int nvar, int nx, int ny, int nz, int dir,
                   const PtrTable &fields, int map, hipStream_t s);
+// SSPRK stage fused with the flux difference: q' = a*q0 + b*(q + dt*rhs).
+struct StageArgs {
+    PtrTable q0, q, qout;  // qout entries are written (the table holds them const)
+    double a, b, dt;
+};
+// rhs != nullptr: write the flux difference; st != nullptr: the stage instead.
 int flux_launch(const PtrTable &fx, const PtrTable &fy, const PtrTable *fz,
                 const double *dx, const double *dy, const double *dz, int nvar,
-                int nx, int ny, int nz, double *rhs, int map, hipStream_t s);
+                int nx, int ny, int nz, double *rhs, const StageArgs *st, int map,
+                hipStream_t s);
 
 }  // namespace sgc

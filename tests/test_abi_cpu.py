@@ -10,7 +10,7 @@ import pytest
 from structured_grid_cfd_amd import binding as b
 
 EXPECTED = ["stencil_diffuse2d", "stencil_diffuse2d_launches", "field_pack", "field_unpack",
-            "flux_diff3d", "sgc_last_error", "sgc_abi_version"]
+            "flux_diff3d", "flux_stage3d", "sgc_last_error", "sgc_abi_version"]
 
 
 @pytest.fixture(scope="module")
@@ -138,6 +138,28 @@ def test_flux_validation(lib):
     assert lib.flux_diff3d(fx, fy, fz, d, d, d, 1, 3000, 3000, 3000, V, 2, None) == 5
     assert lib.flux_diff3d(fx, fy, fz, d, d, d, 1, 4, 4, 4, V + 4, 2, None) == 1
     assert lib.flux_diff3d(_tab(U + 2), fy, fz, d, d, d, 1, 4, 4, 4, V, 2, None) == 1
+
+
+def test_stage_validation(lib):
+    fx, fy, fz = _tab(U), _tab(U + 0x1000), _tab(U + 0x2000)
+    d = U + 0x3000
+    q0, q = _tab(V), _tab(V + 0x1000)
+    def call(qout, a=0.75, b=0.25, dt=0.1, m=2, q0t=q0, qt=q, fzt=fz, dzp=d, n=(4, 4, 4)):
+        return lib.flux_stage3d(fx, fy, fzt, d, d, dzp, q0t, qt, a, b, dt, 1, *n, qout, m, None)
+    assert call(None) == 2
+    assert call(_tab(0)) == 2
+    assert call(_tab(V + 0x3000), q0t=None) == 2
+    assert call(_tab(V + 0x3000), a=float("nan")) == 1 and "finite" in b.last_error()
+    assert call(_tab(V + 0x3000), dt=float("inf")) == 1
+    assert call(_tab(V + 0x3000), m=5) == 1
+    assert call(_tab(V + 0x3000), fzt=None) == 2          # dz given without fz
+    assert call(_tab(V + 0x3000), fzt=None, dzp=None) == 1  # 2D form needs nz == 1
+    assert call(_tab(U + 0x1000)) == 4                     # qout on fy
+    assert call(_tab(d)) == 4                              # qout on the spacings
+    assert call(_tab(V + 8)) == 4                          # qout straddles q0
+    assert call(_tab(V + 0x1000 + 8)) == 4                 # qout straddles q
+    assert call(_tab(V + 4)) == 1                          # misaligned
+    assert call(_tab(V + 0x3000), n=(3000, 3000, 3000)) == 5
 
 
 def test_last_error_is_per_call(lib):

@@ -150,3 +150,22 @@ def test_cfg5_2d_flux_and_packs():
             out = binding.field_pack(fd, direction, map=m)
             torch.cuda.synchronize()
             assert_bitwise(host(out), pref, f"cfg5 pack dir={direction} {m}")
+
+
+def test_cfg4_and_cfg5_flux_stage():
+    """The SSPRK stage fused with the flux difference on the 7 x 201x101x101
+    and 6 x 4800x1200 workloads, in the benchmark's launch configuration."""
+    for fi in (inputs.cfg4(), inputs.cfg5_flux()):
+        nvar, nx, ny, nz = fi.shape
+        g = np.random.Generator(np.random.PCG64(1099))
+        q0 = g.standard_normal((nvar, nz, ny, nx))
+        q = g.standard_normal((nvar, nz, ny, nx))
+        ref = oracle.flux_stage(fi.fx, fi.fy, fi.fz, fi.dx, fi.dy, fi.dz, q0, q, 1.0 / 3.0, 2.0 / 3.0, 1e-3)
+        say("flux stage full size", fi.shape)
+        out = binding.flux_stage3d(dev(fi.fx), dev(fi.fy), dev(fi.fz) if fi.fz is not None else None,
+                                   dev(fi.dx), dev(fi.dy), dev(fi.dz) if fi.dz is not None else None,
+                                   dev(q0), dev(q), 1.0 / 3.0, 2.0 / 3.0, 1e-3, map=launch_config.FLUX["map"])
+        torch.cuda.synchronize()
+        assert_bitwise(host(out), ref, f"stage {fi.shape}")
+        del out
+        torch.cuda.empty_cache()

@@ -140,3 +140,73 @@ def test_pack_and_flux_on_a_nonblocking_stream_are_deterministic():
     assert_bitwise(outs[0][3], oracle.flux_diff(fi.fx, fi.fy, fi.fz, fi.dx, fi.dy, fi.dz), "stream flux")
     for a, b in zip(outs[0], outs[1]):
         assert_bitwise(a, b, "determinism")
+
+
+# ---------------------------------------------------------------------------
+# SSPRK stage fused with the flux difference (flux_stage3d)
+# ---------------------------------------------------------------------------
+
+SSPRK3 = [(0.0, 1.0), (0.75, 0.25), (1.0 / 3.0, 2.0 / 3.0)]
+
+
+def _state(nvar, nx, ny, nz, seed):
+    g = np.random.Generator(np.random.PCG64(seed))
+    return g.standard_normal((nvar, nz, ny, nx)), g.standard_normal((nvar, nz, ny, nx))
+
+
+@pytest.mark.parametrize("nvar,nx,ny,nz,two_d", FLUX_SHAPES)
+def test_flux_stage(nvar, nx, ny, nz, two_d):
+    fi = inputs.normal_faces(nvar, nx, ny, nz, 31 * nvar + nx + ny + nz, two_d)
+    q0, q = _state(nvar, nx, ny, nz, 5 + nx + ny)
+    a, b, dt = 0.75, 0.25, 0.013
+    ref = oracle.flux_stage(fi.fx, fi.fy, fi.fz, fi.dx, fi.dy, fi.dz, q0, q, a, b, dt)
+    args = [dev(fi.fx), dev(fi.fy), dev(fi.fz) if fi.fz is not None else None, dev(fi.dx), dev(fi.dy),
+            dev(fi.dz) if fi.dz is not None else None]
+    for m in MAPS:
+        say("flux stage", nvar, nx, ny, nz, two_d, m)
+        out = binding.flux_stage3d(*args, dev(q0), dev(q), a, b, dt, map=m)
+        torch.cuda.synchronize()
+        assert_bitwise(host(out), ref, f"stage {m}")
+
+
+@pytest.mark.parametrize("m", MAPS)
+def test_flux_stage_in_place_and_ssprk3(m):
+    """q' written over q, then over q0, and a full SSPRK3 step (three stages,
+    each writing in place over the previous stage's state)."""
+    nvar, nx, ny, nz = 4, 67, 45, 23
+    fi = inputs.normal_faces(nvar, nx, ny, nz, 4321)
+    q0, q = _state(nvar, nx, ny, nz, 4322)
+    args = [dev(fi.fx), dev(fi.fy), dev(fi.fz), dev(fi.dx), dev(fi.dy), dev(fi.dz)]
+    ref = oracle.flux_stage(fi.fx, fi.fy, fi.fz, fi.dx, fi.dy, fi.dz, q0, q, 0.75, 0.25, 0.02)
+    say("stage in place", m)
+    q0d, qd = dev(q0), dev(q)
+    binding.flux_stage3d(*args, q0d, qd, 0.75, 0.25, 0.02, out=qd, map=m)
+    torch.cuda.synchronize()
+    assert_bitwise(host(qd), ref, "in place over q")
+    assert_bitwise(host(q0d), q0, "q0 untouched")
+    q0d, qd = dev(q0), dev(q)
+    binding.flux_stage3d(*args, q0d, qd, 0.75, 0.25, 0.02, out=q0d, map=m)
+    torch.cuda.synchronize()
+    assert_bitwise(host(q0d), ref, "in place over q0")
+    # SSPRK3: q1 = stage(q0, q0), q2 = stage(q0, q1), q3 = stage(q0, q2)
+    dt = 0.01
+    qo = q0.copy()
+    for a, b in SSPRK3:
+        qo = oracle.flux_stage(fi.fx, fi.fy, fi.fz, fi.dx, fi.dy, fi.dz, q0, qo, a, b, dt)
+    q0d = dev(q0)
+    qd = q0d.clone()
+    for a, b in SSPRK3:
+        binding.flux_stage3d(*args, q0d, qd, a, b, dt, out=qd, map=m)
+    torch.cuda.synchronize()
+    assert_bitwise(host(qd), qo, f"SSPRK3 {m}")
+
+
+def test_flux_stage_rejects_partial_overlap():
+    fi = inputs.normal_faces(2, 8, 8, 8, 1)
+    q0, q = _state(2, 8, 8, 8, 2)
+    args = [dev(fi.fx), dev(fi.fy), dev(fi.fz), dev(fi.dx), dev(fi.dy), dev(fi.dz)]
+    qd = dev(q)
+    with pytest.raises(binding.SGCError):  # out[0] is q[1]: another variable's state
+        binding.flux_stage3d(*args, dev(q0), qd, 0.5, 0.5, 0.1, out=[qd[1], qd[0]])
+    torch.cuda.synchronize()
+    assert_bitwise(host(qd), q, "q untouched after the rejected call")
