@@ -633,6 +633,11 @@ int launch_march_kv(const void *src, void *dst, const DiffPlan &p, double alpha,
                       : k_march<T, TS, KV, false, kLoadPolicy, kStorePolicy>;
     long rows = p.tile_rows;
     if (rows <= 0) {
+        static SlotCache cache[2];
+        int per_cu = 0, cus = 0;
+        const int rc = resident_slots(reinterpret_cast<const void *>(kernel), cache[vec], &per_cu, &cus);
+        if (rc != SGC_OK) return rc;
+        const long model_rows = march_tile_rows(p.ny, g.nstrips, TS, per_cu, 4L * cus, max_rows);
         if (TS <= 2) {
             rows = 4;  // memory bound: many short tiles in flight
         } else if (TS == 3) {
@@ -641,12 +646,14 @@ int launch_march_kv(const void *src, void *dst, const DiffPlan &p, double alpha,
             // Between memory and ALU bound: about 8192 tiles of 16 to 128 rows.
             rows = max(16L, min((long)p.ny * g.nstrips / 8192, 128L));
         } else {
-            static SlotCache cache[2];
-            int per_cu = 0, cus = 0;
-            const int rc = resident_slots(reinterpret_cast<const void *>(kernel), cache[vec], &per_cu, &cus);
-            if (rc != SGC_OK) return rc;
-            rows = march_tile_rows(p.ny, g.nstrips, TS, per_cu, 4L * cus, max_rows);
+            rows = model_rows;
         }
+        // A grid too small to fill one round of resident waves at the fixed
+        // heights is latency bound: each launch lasts as long as one wave's
+        // march, so it takes the model's height (the shortest tiles that
+        // spread the grid over the resident waves) instead.
+        const long tiles = (long)g.nstrips * ((p.ny + rows - 1) / rows);
+        if (TS <= 4 && tiles < (long)per_cu * 4L * cus) rows = min(rows, model_rows);
     }
     rows = min(rows, (long)p.ny);
     rows = min(rows, max_rows);
