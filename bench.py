@@ -320,7 +320,7 @@ def measure_all(log) -> dict:
     # resident map that runs all sweeps in one workgroup)
     c = inputs.cfg1()
     u, v = dev(c["u"]), dev(c["v"])
-    cfg = launch_config.diffusion("f64")
+    cfg = launch_config.diffusion("f64", 64, 64)
     t = timed(lambda: binding.stencil_diffuse2d(u, v, 64, 0.1, 32, cfg["map"], cfg["time_block"],
                                                 0, stream), 10, False)
     res["diffusion_64_f64_32sweeps"] = entry(t, 62 * 62 * 32, (64 * 64 + 62 * 62) * 8 *
@@ -332,12 +332,15 @@ def measure_all(log) -> dict:
     # size sweep, FP64 production map, 100 sweeps: where the small-grid
     # latency floor gives way to throughput
     for n in (128, 256, 512, 1024, 2048):
+        cfg = launch_config.diffusion("f64", n, n)
         uu, vv = (dev(a) for a in inputs.uniform_grid(n, n, 1100 + n, np.float64))
         fn = lambda: binding.stencil_diffuse2d(uu, vv, n, 0.1, 100, cfg["map"], cfg["time_block"], 0, stream)  # noqa: E731
         fn()
         t = timed(fn, 5, False)
-        res[f"diffusion_{n}_f64_100sweeps"] = entry(t, (n - 2) ** 2 * 100, (n * n + (n - 2) ** 2) * 8 *
-                                                    binding.stencil_diffuse2d_launches(100, cfg["map"], cfg["time_block"]))
+        res[f"diffusion_{n}_f64_100sweeps"] = entry(
+            t, (n - 2) ** 2 * 100, (n * n + (n - 2) ** 2) * 8 *
+            binding.stencil_diffuse2d_launches(100, cfg["map"], cfg["time_block"]),
+            {"time_block": cfg["time_block"]})
         del uu, vv
 
     # 16384^2 FP32, 200 sweeps
