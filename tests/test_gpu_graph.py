@@ -1,0 +1,112 @@
+"""HIP graph capture of the library's calls.
+
+Every entry point only launches kernels on the caller's stream (no memsets,
+no allocations, no synchronisation), so a sequence of calls can be captured
+once and replayed.  Each captured graph is replayed several times with
+ordinary eager work and synchronisations between the replays, from fresh
+inputs each time, and every replay must give the eager call's bits.  The
+first diffusion capture uses a kernel variant no other call in this file
+launches before it (FP32, depth 11, unaligned base), so the launch-shape
+query of a first use happens during capture.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import assert_bitwise, host, require_gpu, say
+from structured_grid_cfd_amd import binding, inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _gpu():
+    require_gpu()
+
+
+def _replays(g, reset, result, ref, what):
+    for rep in range(3):
+        reset()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert_bitwise(host(result()), ref, f"{what} replay {rep}")
+        _ = (torch.ones(1 << 20, device="cuda") * rep).sum().item()  # eager work between replays
+
+
+def _capture(fn):
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        fn()
+    return g
+
+
+@pytest.mark.parametrize("dt,m,tb,off,steps", [
+    (np.float32, "temporal", 11, 1, 33),   # first use of this variant happens under capture
+    (np.float64, "temporal", 10, 0, 40),
+    (np.float64, "tiled", 1, 0, 5),
+    (np.float64, "collapse_branch", 1, 0, 4),
+    (np.float32, "resident", 1, 0, 17),
+])
+def test_diffusion_graph_replays(dt, m, tb, off, steps):
+    nx, ny = (60, 90) if m == "resident" else (700, 300)
+    u0, v0 = inputs.uniform_grid(nx, ny, 1301, dt)
+    say("graph diffusion", m, tb, off, steps)
+    # buffers at an element offset inside larger allocations (off = 1: unaligned base)
+    ub = torch.zeros(ny * nx + 8, dtype=torch.float32 if dt == np.float32 else torch.float64, device="cuda")
+    vb = torch.zeros_like(ub)
+    u = ub[off:off + ny * nx].view(ny, nx)
+    v = vb[off:off + ny * nx].view(ny, nx)
+
+    def reset():
+        u.copy_(torch.from_numpy(u0))
+        v.copy_(torch.from_numpy(v0))
+
+    reset()
+    g = _capture(lambda: binding.stencil_diffuse2d(u, v, nx, 0.1, steps, m, tb))
+    reset()
+    in_v = binding.stencil_diffuse2d(u, v, nx, 0.1, steps, m, tb)
+    torch.cuda.synchronize()
+    ref = host(v if in_v else u).copy()
+    _replays(g, reset, lambda: v if in_v else u, ref, f"diffusion {m}")
+
+
+def test_pack_flux_and_stage_graph_replays():
+    f = inputs.normal_fields(4, 67, 45, 23, 1302)
+    fi = inputs.normal_faces(4, 67, 45, 23, 1303)
+    q0 = inputs.normal_fields(4, 67, 45, 23, 1304)
+    fd = torch.from_numpy(f).cuda()
+    args = [torch.from_numpy(a).cuda() for a in (fi.fx, fi.fy, fi.fz, fi.dx, fi.dy, fi.dz)]
+    q0d = torch.from_numpy(q0).cuda()
+    qd = q0d.clone()
+    outs = [torch.empty(f.size, dtype=torch.float64, device="cuda") for _ in range(3)]
+    rhs = torch.empty_like(q0d)
+    say("graph pack/flux/stage")
+
+    def calls():
+        for d in range(3):
+            binding.field_pack(fd, d, out=outs[d])
+        binding.flux_diff3d(*args, rhs=rhs)
+        binding.flux_stage3d(*args, q0d, qd, 0.75, 0.25, 0.01, out=qd)  # in place
+
+    def reset():
+        qd.copy_(q0d)
+        for o in outs:
+            o.zero_()
+        rhs.zero_()
+
+    reset()
+    g = _capture(calls)
+    reset()
+    calls()
+    torch.cuda.synchronize()
+    refs = [host(o).copy() for o in outs] + [host(rhs).copy(), host(qd).copy()]
+    for rep in range(3):
+        reset()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, ref in zip([host(o) for o in outs] + [host(rhs), host(qd)], refs):
+            assert_bitwise(got, ref, f"pack/flux/stage replay {rep}")
