@@ -1,4 +1,5 @@
-"""HIP graph capture of the library's calls.
+"""HIP graph capture of the library's calls, and concurrent calls from
+several host threads.
 
 Every entry point only launches kernels on the caller's stream (no memsets,
 no allocations, no synchronisation), so a sequence of calls can be captured
@@ -110,3 +111,43 @@ def test_pack_flux_and_stage_graph_replays():
         torch.cuda.synchronize()
         for got, ref in zip([host(o) for o in outs] + [host(rhs), host(qd)], refs):
             assert_bitwise(got, ref, f"pack/flux/stage replay {rep}")
+
+
+def test_concurrent_host_threads_on_separate_streams():
+    """Four host threads call the library at once, each on its own stream
+    and buffers (the launch-shape cache is shared, the error state is per
+    thread); every result is the oracle's."""
+    import threading
+
+    import oracle
+    cases = [(np.float64, 300 + 37 * k, 200 + 11 * k, 10 + k, 1400 + k) for k in range(4)]
+    refs = [oracle.diffuse2d_result(inputs.uniform_grid(nx, ny, seed, dt)[0], nx, 0.1, steps)
+            for dt, nx, ny, steps, seed in cases]
+    outs, errors = [None] * 4, []
+
+    def work(k):
+        try:
+            dt, nx, ny, steps, seed = cases[k]
+            u0, v0 = inputs.uniform_grid(nx, ny, seed, dt)
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                u, v = torch.from_numpy(u0).cuda(), torch.from_numpy(v0).cuda()
+                s.synchronize()
+                for _ in range(3):  # repeated calls interleave with the other threads'
+                    u.copy_(torch.from_numpy(u0))
+                    v.copy_(torch.from_numpy(v0))
+                    in_v = binding.stencil_diffuse2d(u, v, nx, 0.1, steps, "temporal", 4 + k, 0, s)
+                s.synchronize()
+                outs[k] = host(v if in_v else u).copy()
+        except Exception as e:  # noqa: BLE001 -- reported by the main thread
+            errors.append(repr(e))
+
+    say("concurrent host threads")
+    threads = [threading.Thread(target=work, args=(k,)) for k in range(4)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not errors, errors
+    for k in range(4):
+        assert_bitwise(outs[k], refs[k], f"thread {k}")
