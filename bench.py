@@ -67,6 +67,10 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-steps", type=int, default=1000,
                    help="sweeps of the CPU-baseline sample (same grid; 1000 = one full step, ~11 s)")
+    p.add_argument("--kernels", default="all",
+                   help="comma-separated sections of the per-kernel table: copy, diffusion "
+                        "(4096^2), small (64^2 and the size sweep), large (16384^2), pack, flux, "
+                        "2d (4800x1200 flux and packs), or all")
     p.add_argument("--ref-copy", action="store_true",
                    help="first run one 1 GiB copy (1 GiB read + 1 GiB written) as a known-size "
                         "reference for profiler byte counters")
@@ -75,6 +79,16 @@ def parse():
 
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def host_cpu_model() -> str:
+    try:
+        for line in Path("/proc/cpuinfo").read_text().splitlines():
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "host CPU"
 
 
 def source_hash(path: Path) -> str:
@@ -186,22 +200,30 @@ def main():
     if not args.no_cpu:
         import oracle
         uc, vc = c["u"].copy(), c["v"].copy()
-        log(f"cpu baseline: oracle, {args.cpu_steps} sweeps of the same grid, one thread")
-        t = time.perf_counter()
-        oracle.diffuse2d(uc, vc, nx, c["alpha"], args.cpu_steps)
-        dt = time.perf_counter() - t
+        # pinned to one core of this process's set for the duration of the call
+        allowed = os.sched_getaffinity(0)
+        core = min(allowed)
+        log(f"cpu baseline: oracle, {args.cpu_steps} sweeps of the same grid, one thread on core {core}")
+        os.sched_setaffinity(0, {core})
+        try:
+            t = time.perf_counter()
+            oracle.diffuse2d(uc, vc, nx, c["alpha"], args.cpu_steps)
+            dt = time.perf_counter() - t
+        finally:
+            os.sched_setaffinity(0, allowed)
         cpu = {"value": (nx - 2) * (ny - 2) * args.cpu_steps / dt, "unit": "cell-var updates/s",
                "cores": 1, "kind": "oracle",
                "sample": f"{nx}x{ny} {args.dtype}, {args.cpu_steps} of the {sweeps} sweeps of one "
-                         f"step, single-threaded C oracle ({dt:.1f} s on {platform.processor() or 'host'}"
-                         f", {os.cpu_count()} host cores visible)"}
+                         f"step, single-threaded C oracle pinned to one core ({dt:.1f} s on "
+                         f"{host_cpu_model()}, {len(allowed)} of {os.cpu_count()} host cores "
+                         f"available to the process)"}
         log(f"cpu baseline: {cpu['value']:.4e} cell-updates/s in {dt:.1f} s")
 
     kernels = None
     if not args.quick:
         del u, v
         torch.cuda.empty_cache()
-        kernels = measure_all(log)
+        kernels = measure_all(log, set(args.kernels.split(",")))
 
     line = {
         "metric": METRIC, "value": value, "unit": "cell-var updates/s", "n_gpus": 1,
@@ -226,10 +248,13 @@ def main():
 # Per-kernel table (secondary figures; the JSON line's `kernels` object)
 # ---------------------------------------------------------------------------
 
-def measure_all(log) -> dict:
+def measure_all(log, sections=frozenset({"all"})) -> dict:
     import torch
 
     from structured_grid_cfd_amd import binding, inputs, launch_config
+
+    def want(name):
+        return "all" in sections or name in sections
 
     stream = torch.cuda.current_stream()
     flush_buf = torch.ones(256 * 1024 * 1024, dtype=torch.float32, device="cuda")  # 1 GiB
@@ -266,175 +291,183 @@ def measure_all(log) -> dict:
     res = {}
     dev = lambda a: torch.from_numpy(a).cuda()  # noqa: E731
 
-    # reference: a 16-byte-vector copy of 1 GiB (the x pack of one variable)
-    n = 128 * 1024 * 1024
-    src = torch.empty((1, 1, 1, n), dtype=torch.float64, device="cuda").fill_(1.0)
-    dst = torch.empty_like(src)
-    binding.field_pack(src, 0, out=dst)
-    t = timed(lambda: binding.field_pack(src, 0, out=dst), 5, True)
-    res["copy_1GiB_dwordx4"] = entry(t, n, 2 * n * 8)
-    log("copy", res["copy_1GiB_dwordx4"])
-    del src, dst
+    if want("copy"):
+        # reference: a 16-byte-vector copy of 1 GiB (the x pack of one variable)
+        n = 128 * 1024 * 1024
+        src = torch.empty((1, 1, 1, n), dtype=torch.float64, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        binding.field_pack(src, 0, out=dst)
+        t = timed(lambda: binding.field_pack(src, 0, out=dst), 5, True)
+        res["copy_1GiB_dwordx4"] = entry(t, n, 2 * n * 8)
+        log("copy", res["copy_1GiB_dwordx4"])
+        del src, dst
 
-    # diffusion, 4096^2: production in both precisions, the page layouts, time blocks
-    for dt_name, dt in (("f64", np.float64), ("f32", np.float32)):
-        es = 8 if dt_name == "f64" else 4
-        c = inputs.cfg2(dt)
-        nx, ny = c["nx"], c["ny"]
-        per_sweep = (nx * ny + (nx - 2) * (ny - 2)) * es
-        u0, v0 = dev(c["u"]), dev(c["v"])
-        u, v = u0.clone(), v0.clone()
-        cells = (nx - 2) * (ny - 2)
+    if want("diffusion"):
+        # diffusion, 4096^2: production in both precisions, the page layouts, time blocks
+        for dt_name, dt in (("f64", np.float64), ("f32", np.float32)):
+            es = 8 if dt_name == "f64" else 4
+            c = inputs.cfg2(dt)
+            nx, ny = c["nx"], c["ny"]
+            per_sweep = (nx * ny + (nx - 2) * (ny - 2)) * es
+            u0, v0 = dev(c["u"]), dev(c["v"])
+            u, v = u0.clone(), v0.clone()
+            cells = (nx - 2) * (ny - 2)
 
-        def run(m, tb, sweeps, rows=0):
-            binding.stencil_diffuse2d(u, v, nx, 0.1, sweeps, m, tb, rows, stream)
+            def run(m, tb, sweeps, rows=0):
+                binding.stencil_diffuse2d(u, v, nx, 0.1, sweeps, m, tb, rows, stream)
 
-        cfg = launch_config.diffusion(dt_name)
-        run(cfg["map"], cfg["time_block"], 1000, cfg["tile_rows"])
-        t = timed(lambda: run(cfg["map"], cfg["time_block"], 1000, cfg["tile_rows"]), 3, False)
-        L = binding.stencil_diffuse2d_launches(1000, cfg["map"], cfg["time_block"])
-        res[f"diffusion_4096_{dt_name}_1000sweeps_production"] = entry(
-            t, cells * 1000, per_sweep * L,
-            {"map": cfg["map"], "time_block": cfg["time_block"], "launches": L,
-             "note": "gbs_minimal counts one grid read + write per launch"})
-        log(dt_name, "production", res[f"diffusion_4096_{dt_name}_1000sweeps_production"])
-        for m in ("collapse_branch", "contig", "strided", "tiled"):
-            sw = 100
-            run(m, 1, 2)
-            t = timed(lambda: run(m, 1, sw), 3, False)
-            res[f"diffusion_4096_{dt_name}_{m}"] = entry(t, cells * sw, per_sweep * sw,
-                                                         {"sweeps": sw})
-            log(dt_name, m, res[f"diffusion_4096_{dt_name}_{m}"])
-        for tb in (2, 3, 4, 6, 8, 10, 12):
-            sw = 240
-            run("temporal", tb, sw)
-            t = timed(lambda: run("temporal", tb, sw), 3, False)
-            L = binding.stencil_diffuse2d_launches(sw, "temporal", tb)
-            res[f"diffusion_4096_{dt_name}_temporal_T{tb}"] = entry(
-                t, cells * sw, per_sweep * L, {"sweeps": sw, "launches": L})
-            log(dt_name, "T", tb, res[f"diffusion_4096_{dt_name}_temporal_T{tb}"])
-        del u, v, u0, v0
+            cfg = launch_config.diffusion(dt_name)
+            run(cfg["map"], cfg["time_block"], 1000, cfg["tile_rows"])
+            t = timed(lambda: run(cfg["map"], cfg["time_block"], 1000, cfg["tile_rows"]), 3, False)
+            L = binding.stencil_diffuse2d_launches(1000, cfg["map"], cfg["time_block"])
+            res[f"diffusion_4096_{dt_name}_1000sweeps_production"] = entry(
+                t, cells * 1000, per_sweep * L,
+                {"map": cfg["map"], "time_block": cfg["time_block"], "launches": L,
+                 "note": "gbs_minimal counts one grid read + write per launch"})
+            log(dt_name, "production", res[f"diffusion_4096_{dt_name}_1000sweeps_production"])
+            for m in ("collapse_branch", "contig", "strided", "tiled"):
+                sw = 100
+                run(m, 1, 2)
+                t = timed(lambda: run(m, 1, sw), 3, False)
+                res[f"diffusion_4096_{dt_name}_{m}"] = entry(t, cells * sw, per_sweep * sw,
+                                                             {"sweeps": sw})
+                log(dt_name, m, res[f"diffusion_4096_{dt_name}_{m}"])
+            for tb in (2, 3, 4, 6, 8, 10, 12):
+                sw = 240
+                run("temporal", tb, sw)
+                t = timed(lambda: run("temporal", tb, sw), 3, False)
+                L = binding.stencil_diffuse2d_launches(sw, "temporal", tb)
+                res[f"diffusion_4096_{dt_name}_temporal_T{tb}"] = entry(
+                    t, cells * sw, per_sweep * L, {"sweeps": sw, "launches": L})
+                log(dt_name, "T", tb, res[f"diffusion_4096_{dt_name}_temporal_T{tb}"])
+            del u, v, u0, v0
+            torch.cuda.empty_cache()
+
+    if want("small"):
+        # 64x64 impulse, 32 sweeps: launch/latency bound (production march, and the
+        # resident map that runs all sweeps in one workgroup)
+        c = inputs.cfg1()
+        u, v = dev(c["u"]), dev(c["v"])
+        cfg = launch_config.diffusion("f64", 64, 64)
+        t = timed(lambda: binding.stencil_diffuse2d(u, v, 64, 0.1, 32, cfg["map"], cfg["time_block"],
+                                                    0, stream), 10, False)
+        res["diffusion_64_f64_32sweeps"] = entry(t, 62 * 62 * 32, (64 * 64 + 62 * 62) * 8 *
+                                                 binding.stencil_diffuse2d_launches(32, cfg["map"], cfg["time_block"]))
+        t = timed(lambda: binding.stencil_diffuse2d(u, v, 64, 0.1, 32, "resident", 1, 0, stream), 10, False)
+        res["diffusion_64_f64_32sweeps_resident"] = entry(t, 62 * 62 * 32, (64 * 64 + 62 * 62) * 8,
+                                                          {"map": "resident", "launches": 1})
+
+        # size sweep, FP64 production map, 100 sweeps: where the small-grid
+        # latency floor gives way to throughput
+        for n in (128, 256, 512, 1024, 2048):
+            cfg = launch_config.diffusion("f64", n, n)
+            uu, vv = (dev(a) for a in inputs.uniform_grid(n, n, 1100 + n, np.float64))
+            fn = lambda: binding.stencil_diffuse2d(uu, vv, n, 0.1, 100, cfg["map"], cfg["time_block"], 0, stream)  # noqa: E731
+            fn()
+            t = timed(fn, 5, False)
+            res[f"diffusion_{n}_f64_100sweeps"] = entry(
+                t, (n - 2) ** 2 * 100, (n * n + (n - 2) ** 2) * 8 *
+                binding.stencil_diffuse2d_launches(100, cfg["map"], cfg["time_block"]),
+                {"time_block": cfg["time_block"]})
+            del uu, vv
+
+    if want("large"):
+        # 16384^2 FP32, 200 sweeps
+        c = inputs.cfg5_diffusion()
+        u, v = dev(c["u"]), dev(c["v"])
+        del c
+        cfg = launch_config.diffusion("f32")
+        nx = ny = 16384
+        binding.stencil_diffuse2d(u, v, nx, 0.1, 8, cfg["map"], cfg["time_block"], 0, stream)
+        t = timed(lambda: binding.stencil_diffuse2d(u, v, nx, 0.1, 200, cfg["map"], cfg["time_block"],
+                                                    cfg["tile_rows"], stream), 2, False)
+        L = binding.stencil_diffuse2d_launches(200, cfg["map"], cfg["time_block"])
+        res["diffusion_16384_f32_200sweeps_production"] = entry(
+            t, (nx - 2) * (ny - 2) * 200, (nx * ny + (nx - 2) * (ny - 2)) * 4 * L,
+            {"launches": L, "time_block": cfg["time_block"]})
+        log("16384", res["diffusion_16384_f32_200sweeps_production"])
+        t = timed(lambda: binding.stencil_diffuse2d(u, v, nx, 0.1, 10, "tiled", 1, 0, stream), 2, False)
+        res["diffusion_16384_f32_tiled_single_sweep"] = entry(
+            t, (nx - 2) * (ny - 2) * 10, (nx * ny + (nx - 2) * (ny - 2)) * 4 * 10, {"sweeps": 10})
+        log("16384 tiled", res["diffusion_16384_f32_tiled_single_sweep"])
+        del u, v
         torch.cuda.empty_cache()
 
-    # 64x64 impulse, 32 sweeps: launch/latency bound (production march, and the
-    # resident map that runs all sweeps in one workgroup)
-    c = inputs.cfg1()
-    u, v = dev(c["u"]), dev(c["v"])
-    cfg = launch_config.diffusion("f64", 64, 64)
-    t = timed(lambda: binding.stencil_diffuse2d(u, v, 64, 0.1, 32, cfg["map"], cfg["time_block"],
-                                                0, stream), 10, False)
-    res["diffusion_64_f64_32sweeps"] = entry(t, 62 * 62 * 32, (64 * 64 + 62 * 62) * 8 *
-                                             binding.stencil_diffuse2d_launches(32, cfg["map"], cfg["time_block"]))
-    t = timed(lambda: binding.stencil_diffuse2d(u, v, 64, 0.1, 32, "resident", 1, 0, stream), 10, False)
-    res["diffusion_64_f64_32sweeps_resident"] = entry(t, 62 * 62 * 32, (64 * 64 + 62 * 62) * 8,
-                                                      {"map": "resident", "launches": 1})
+    if want("pack"):
+        # pack, 8 x 201^3
+        f = dev(inputs.cfg3())
+        nvar, nz, ny_, nx_ = f.shape
+        cv = nvar * nx_ * ny_ * nz
+        out = torch.empty(cv, dtype=torch.float64, device="cuda")
+        for d, dn in enumerate("xyz"):
+            for m in ("tiled", "per_cell", "per_cellvar"):
+                binding.field_pack(f, d, out=out, map=m)
+                t = timed(lambda: binding.field_pack(f, d, out=out, map=m), 5, True)
+                res[f"pack_201cubed_x8_{dn}_{m}"] = entry(t, cv, 16 * cv)
+                log("pack", dn, m, res[f"pack_201cubed_x8_{dn}_{m}"])
+        del f, out
+        torch.cuda.empty_cache()
 
-    # size sweep, FP64 production map, 100 sweeps: where the small-grid
-    # latency floor gives way to throughput
-    for n in (128, 256, 512, 1024, 2048):
-        cfg = launch_config.diffusion("f64", n, n)
-        uu, vv = (dev(a) for a in inputs.uniform_grid(n, n, 1100 + n, np.float64))
-        fn = lambda: binding.stencil_diffuse2d(uu, vv, n, 0.1, 100, cfg["map"], cfg["time_block"], 0, stream)  # noqa: E731
-        fn()
-        t = timed(fn, 5, False)
-        res[f"diffusion_{n}_f64_100sweeps"] = entry(
-            t, (n - 2) ** 2 * 100, (n * n + (n - 2) ** 2) * 8 *
-            binding.stencil_diffuse2d_launches(100, cfg["map"], cfg["time_block"]),
-            {"time_block": cfg["time_block"]})
-        del uu, vv
-
-    # 16384^2 FP32, 200 sweeps
-    c = inputs.cfg5_diffusion()
-    u, v = dev(c["u"]), dev(c["v"])
-    del c
-    cfg = launch_config.diffusion("f32")
-    nx = ny = 16384
-    binding.stencil_diffuse2d(u, v, nx, 0.1, 8, cfg["map"], cfg["time_block"], 0, stream)
-    t = timed(lambda: binding.stencil_diffuse2d(u, v, nx, 0.1, 200, cfg["map"], cfg["time_block"],
-                                                cfg["tile_rows"], stream), 2, False)
-    L = binding.stencil_diffuse2d_launches(200, cfg["map"], cfg["time_block"])
-    res["diffusion_16384_f32_200sweeps_production"] = entry(
-        t, (nx - 2) * (ny - 2) * 200, (nx * ny + (nx - 2) * (ny - 2)) * 4 * L,
-        {"launches": L, "time_block": cfg["time_block"]})
-    log("16384", res["diffusion_16384_f32_200sweeps_production"])
-    t = timed(lambda: binding.stencil_diffuse2d(u, v, nx, 0.1, 10, "tiled", 1, 0, stream), 2, False)
-    res["diffusion_16384_f32_tiled_single_sweep"] = entry(
-        t, (nx - 2) * (ny - 2) * 10, (nx * ny + (nx - 2) * (ny - 2)) * 4 * 10, {"sweeps": 10})
-    log("16384 tiled", res["diffusion_16384_f32_tiled_single_sweep"])
-    del u, v
-    torch.cuda.empty_cache()
-
-    # pack, 8 x 201^3
-    f = dev(inputs.cfg3())
-    nvar, nz, ny_, nx_ = f.shape
-    cv = nvar * nx_ * ny_ * nz
-    out = torch.empty(cv, dtype=torch.float64, device="cuda")
-    for d, dn in enumerate("xyz"):
+    if want("flux"):
+        # flux difference, 7 x 201x101x101
+        fi = inputs.cfg4()
+        args = (dev(fi.fx), dev(fi.fy), dev(fi.fz), dev(fi.dx), dev(fi.dy), dev(fi.dz))
+        nvar, nxc, nyc, nzc = fi.shape
+        cv = nvar * nxc * nyc * nzc
+        nbytes = 8 * (fi.fx.size + fi.fy.size + fi.fz.size + cv + nxc + nyc + nzc)
+        rhs = torch.empty(cv, dtype=torch.float64, device="cuda").view(nvar, nzc, nyc, nxc)
         for m in ("tiled", "per_cell", "per_cellvar"):
-            binding.field_pack(f, d, out=out, map=m)
-            t = timed(lambda: binding.field_pack(f, d, out=out, map=m), 5, True)
-            res[f"pack_201cubed_x8_{dn}_{m}"] = entry(t, cv, 16 * cv)
-            log("pack", dn, m, res[f"pack_201cubed_x8_{dn}_{m}"])
-    del f, out
-    torch.cuda.empty_cache()
-
-    # flux difference, 7 x 201x101x101
-    fi = inputs.cfg4()
-    args = (dev(fi.fx), dev(fi.fy), dev(fi.fz), dev(fi.dx), dev(fi.dy), dev(fi.dz))
-    nvar, nxc, nyc, nzc = fi.shape
-    cv = nvar * nxc * nyc * nzc
-    nbytes = 8 * (fi.fx.size + fi.fy.size + fi.fz.size + cv + nxc + nyc + nzc)
-    rhs = torch.empty(cv, dtype=torch.float64, device="cuda").view(nvar, nzc, nyc, nxc)
-    for m in ("tiled", "per_cell", "per_cellvar"):
-        binding.flux_diff3d(*args, rhs=rhs, map=m)
-        t = timed(lambda: binding.flux_diff3d(*args, rhs=rhs, map=m), 5, True)
-        res[f"flux_201x101x101_x7_{m}"] = entry(t, cv, nbytes)
-        log("flux", m, res[f"flux_201x101x101_x7_{m}"])
-    # one SSPRK stage fused with it: reads q0 and q, writes q' instead of rhs
-    q0 = dev(inputs.normal_fields(nvar, nxc, nyc, nzc, 1060))
-    qs = dev(inputs.normal_fields(nvar, nxc, nyc, nzc, 1061))
-    qo = torch.empty_like(qs)
-    sbytes = nbytes + 2 * 8 * cv
-    for m in ("tiled", "per_cell", "per_cellvar"):
-        binding.flux_stage3d(*args, q0, qs, 0.75, 0.25, 1e-3, out=qo, map=m)
-        t = timed(lambda: binding.flux_stage3d(*args, q0, qs, 0.75, 0.25, 1e-3, out=qo, map=m), 5, True)
-        res[f"flux_stage_201x101x101_x7_{m}"] = entry(
-            t, cv, sbytes, {"note": "a separate update pass would add one write and one read of rhs"})
-        log("flux stage", m, res[f"flux_stage_201x101x101_x7_{m}"])
-    del args, rhs, q0, qs, qo
-    torch.cuda.empty_cache()
-
-    # 2D workload, 6 x 4800x1200: flux difference and packs along x, y
-    fi = inputs.cfg5_flux()
-    args = (dev(fi.fx), dev(fi.fy), None, dev(fi.dx), dev(fi.dy), None)
-    nvar, nxc, nyc, _ = fi.shape
-    cv = nvar * nxc * nyc
-    nbytes = 8 * (fi.fx.size + fi.fy.size + cv + nxc + nyc)
-    rhs = torch.empty(cv, dtype=torch.float64, device="cuda").view(nvar, 1, nyc, nxc)
-    for m in ("tiled", "per_cell", "per_cellvar"):
-        binding.flux_diff3d(*args, rhs=rhs, map=m)
-        t = timed(lambda: binding.flux_diff3d(*args, rhs=rhs, map=m), 5, True)
-        res[f"flux2d_4800x1200_x6_{m}"] = entry(t, cv, nbytes)
-        log("flux2d", m, res[f"flux2d_4800x1200_x6_{m}"])
-    q0 = dev(inputs.normal_fields(nvar, nxc, nyc, 1, 1062))
-    qs = dev(inputs.normal_fields(nvar, nxc, nyc, 1, 1063))
-    qo = torch.empty_like(qs)
-    sbytes = nbytes + 2 * 8 * cv
-    binding.flux_stage3d(*args, q0, qs, 0.75, 0.25, 1e-3, out=qo)
-    t = timed(lambda: binding.flux_stage3d(*args, q0, qs, 0.75, 0.25, 1e-3, out=qo), 5, True)
-    res["flux_stage2d_4800x1200_x6_tiled"] = entry(t, cv, sbytes)
-    log("flux2d stage", res["flux_stage2d_4800x1200_x6_tiled"])
-    del args, rhs, q0, qs, qo
-    f = dev(inputs.cfg5_fields())
-    out = torch.empty(cv, dtype=torch.float64, device="cuda")
-    for d, dn in ((0, "x"), (1, "y")):
+            binding.flux_diff3d(*args, rhs=rhs, map=m)
+            t = timed(lambda: binding.flux_diff3d(*args, rhs=rhs, map=m), 5, True)
+            res[f"flux_201x101x101_x7_{m}"] = entry(t, cv, nbytes)
+            log("flux", m, res[f"flux_201x101x101_x7_{m}"])
+        # one SSPRK stage fused with it: reads q0 and q, writes q' instead of rhs
+        q0 = dev(inputs.normal_fields(nvar, nxc, nyc, nzc, 1060))
+        qs = dev(inputs.normal_fields(nvar, nxc, nyc, nzc, 1061))
+        qo = torch.empty_like(qs)
+        sbytes = nbytes + 2 * 8 * cv
         for m in ("tiled", "per_cell", "per_cellvar"):
-            binding.field_pack(f, d, out=out, map=m)
-            t = timed(lambda: binding.field_pack(f, d, out=out, map=m), 5, True)
-            res[f"pack2d_4800x1200_x6_{dn}_{m}"] = entry(t, cv, 16 * cv)
-            log("pack2d", dn, m, res[f"pack2d_4800x1200_x6_{dn}_{m}"])
-    del f, out, flush_buf
-    torch.cuda.empty_cache()
+            binding.flux_stage3d(*args, q0, qs, 0.75, 0.25, 1e-3, out=qo, map=m)
+            t = timed(lambda: binding.flux_stage3d(*args, q0, qs, 0.75, 0.25, 1e-3, out=qo, map=m), 5, True)
+            res[f"flux_stage_201x101x101_x7_{m}"] = entry(
+                t, cv, sbytes, {"note": "a separate update pass would add one write and one read of rhs"})
+            log("flux stage", m, res[f"flux_stage_201x101x101_x7_{m}"])
+        del args, rhs, q0, qs, qo
+        torch.cuda.empty_cache()
+
+    if want("2d"):
+        # 2D workload, 6 x 4800x1200: flux difference and packs along x, y
+        fi = inputs.cfg5_flux()
+        args = (dev(fi.fx), dev(fi.fy), None, dev(fi.dx), dev(fi.dy), None)
+        nvar, nxc, nyc, _ = fi.shape
+        cv = nvar * nxc * nyc
+        nbytes = 8 * (fi.fx.size + fi.fy.size + cv + nxc + nyc)
+        rhs = torch.empty(cv, dtype=torch.float64, device="cuda").view(nvar, 1, nyc, nxc)
+        for m in ("tiled", "per_cell", "per_cellvar"):
+            binding.flux_diff3d(*args, rhs=rhs, map=m)
+            t = timed(lambda: binding.flux_diff3d(*args, rhs=rhs, map=m), 5, True)
+            res[f"flux2d_4800x1200_x6_{m}"] = entry(t, cv, nbytes)
+            log("flux2d", m, res[f"flux2d_4800x1200_x6_{m}"])
+        q0 = dev(inputs.normal_fields(nvar, nxc, nyc, 1, 1062))
+        qs = dev(inputs.normal_fields(nvar, nxc, nyc, 1, 1063))
+        qo = torch.empty_like(qs)
+        sbytes = nbytes + 2 * 8 * cv
+        binding.flux_stage3d(*args, q0, qs, 0.75, 0.25, 1e-3, out=qo)
+        t = timed(lambda: binding.flux_stage3d(*args, q0, qs, 0.75, 0.25, 1e-3, out=qo), 5, True)
+        res["flux_stage2d_4800x1200_x6_tiled"] = entry(t, cv, sbytes)
+        log("flux2d stage", res["flux_stage2d_4800x1200_x6_tiled"])
+        del args, rhs, q0, qs, qo
+        f = dev(inputs.cfg5_fields())
+        out = torch.empty(cv, dtype=torch.float64, device="cuda")
+        for d, dn in ((0, "x"), (1, "y")):
+            for m in ("tiled", "per_cell", "per_cellvar"):
+                binding.field_pack(f, d, out=out, map=m)
+                t = timed(lambda: binding.field_pack(f, d, out=out, map=m), 5, True)
+                res[f"pack2d_4800x1200_x6_{dn}_{m}"] = entry(t, cv, 16 * cv)
+                log("pack2d", dn, m, res[f"pack2d_4800x1200_x6_{dn}_{m}"])
+        del f, out
+        torch.cuda.empty_cache()
+    del flush_buf
     return res
 
 
