@@ -23,6 +23,8 @@
 //     drops stores outside the wave's rows, so the loop has no branches around
 //     memory and its prefetch waits stay partial.
 #include <atomic>
+#include <climits>
+#include <cmath>
 
 #include "sgc_internal.h"
 
@@ -211,6 +213,7 @@ struct MarchArgs {
     int tile_rows;  // output rows per tile
     double alpha;
     double fuse_limit;  // fused form allowed while sum |input| stays below this
+    int balance;        // waves lower their issue priority as they progress
 };
 
 // Strip geometry for KV lane vectors per lane: K = KV*V columns per lane,
@@ -236,7 +239,7 @@ template <typename T, int KV> constexpr int march_out_width(int ts) {
 template <typename T, int TS, int KV, bool VEC, bool EDGE, bool DOWN, int LPOL, int SPOL, bool FUSED>
 __device__ __forceinline__ bool march(const T *__restrict__ src, T *__restrict__ dst, int nx,
                                       int ny, int ld, T a, T limit, int lane, int col_out0,
-                                      int row_out0, int row_out1) {
+                                      int row_out0, int row_out1, bool balance) {
     constexpr int V = lane_elems<T>(TS);
     constexpr int K = march_k<T, KV>(TS);
     constexpr int HALO = march_halo<T, KV>(TS);
@@ -373,7 +376,32 @@ __device__ __forceinline__ bool march(const T *__restrict__ src, T *__restrict__
         }
     };
 
+    // Issue priority falls as the march nears its end: 3 for the first half
+    // of the rows, then 2, 1 and 0 from 1/2, 3/4 and 7/8 of the way.  The
+    // SIMD's arbiter otherwise favours its oldest wave, which then finishes
+    // well ahead of the others and leaves the last one to run alone at a
+    // fraction of the VALU rate for the end of the launch; with falling
+    // priority, waves that are ahead yield to those behind and the waves of
+    // a SIMD finish close together.  A launch with fewer than two waves per
+    // SIMD has nothing to balance and keeps the default priority.
+    // One compare per iteration: `next` is the iteration of the next drop.
+    int prio = 3;
+    int next = balance ? nit3 / 2 : INT_MAX;
+    if (balance) __builtin_amdgcn_s_setprio(3);
     for (int it = 0; it < nit3; it += 3) {
+        if (it >= next) {
+            --prio;
+            if (prio == 2) {
+                __builtin_amdgcn_s_setprio(2);
+                next = nit3 * 3 / 4;
+            } else if (prio == 1) {
+                __builtin_amdgcn_s_setprio(1);
+                next = nit3 * 7 / 8;
+            } else {
+                __builtin_amdgcn_s_setprio(0);
+                next = INT_MAX;
+            }
+        }
         step(std::integral_constant<int, 0>{}, it);
         step(std::integral_constant<int, 1>{}, it + 1);
         step(std::integral_constant<int, 2>{}, it + 2);
@@ -414,24 +442,24 @@ __global__ __launch_bounds__(256) void k_march(MarchArgs g) {
     if (rtile & 1) {
         if (interior) {
             const bool redo = march<T, TS, KV, VEC, false, true, LPOL, SPOL, true>(
-                src, dst, g.nx, g.ny, g.ld, a, limit, lane, col_out0, row_out0, row_out1);
+                src, dst, g.nx, g.ny, g.ld, a, limit, lane, col_out0, row_out0, row_out1, g.balance != 0);
             if (__any(redo))
                 march<T, TS, KV, VEC, true, true, LPOL, SPOL, false>(
-                    src, dst, g.nx, g.ny, g.ld, a, limit, lane, col_out0, row_out0, row_out1);
+                    src, dst, g.nx, g.ny, g.ld, a, limit, lane, col_out0, row_out0, row_out1, g.balance != 0);
         } else {
             march<T, TS, KV, VEC, true, true, LPOL, SPOL, false>(src, dst, g.nx, g.ny, g.ld, a, limit,
-                                                                 lane, col_out0, row_out0, row_out1);
+                                                                 lane, col_out0, row_out0, row_out1, g.balance != 0);
         }
     } else {
         if (interior) {
             const bool redo = march<T, TS, KV, VEC, false, false, LPOL, SPOL, true>(
-                src, dst, g.nx, g.ny, g.ld, a, limit, lane, col_out0, row_out0, row_out1);
+                src, dst, g.nx, g.ny, g.ld, a, limit, lane, col_out0, row_out0, row_out1, g.balance != 0);
             if (__any(redo))
                 march<T, TS, KV, VEC, true, false, LPOL, SPOL, false>(
-                    src, dst, g.nx, g.ny, g.ld, a, limit, lane, col_out0, row_out0, row_out1);
+                    src, dst, g.nx, g.ny, g.ld, a, limit, lane, col_out0, row_out0, row_out1, g.balance != 0);
         } else {
             march<T, TS, KV, VEC, true, false, LPOL, SPOL, false>(src, dst, g.nx, g.ny, g.ld, a, limit,
-                                                                  lane, col_out0, row_out0, row_out1);
+                                                                  lane, col_out0, row_out0, row_out1, g.balance != 0);
         }
     }
 }
@@ -524,13 +552,15 @@ template <typename T> constexpr int vectors_per_lane(int) { return 1; }
 // wave on some SIMDs, or start a short extra round, and sweeps show those
 // 10-30% slower; so each candidate takes the lowest height whose tile count
 // fits w waves per SIMD exactly, for w = 1..occupancy (one round) and for
-// whole rounds of `occupancy` waves, and the cheapest candidate wins.  Tiles
-// taller than 128 rows measured 3-7% slower on grids too large to stay in
-// the on-package cache, so taller candidates are left out.  Efficiency of a
-// SIMD running w march waves, relative to four, from sweeps over
-// 2048^2..16384^2 grids at depths 6-10 in FP64 and FP32 on MI355X:
-constexpr double kWaveEfficiency[] = {0.0, 0.55, 0.85, 0.95, 1.0};
-constexpr long kMaxTileRows = 128;
+// whole rounds of `occupancy` waves, and the cheapest candidate wins.  The
+// efficiency of w resident waves relative to a full SIMD fits (w/occupancy)^0.7
+// in sweeps over 2048^2..16384^2 grids at depths 8-10 in FP64 and FP32 on
+// MI355X (waves with falling issue priority, as the march sets it): one
+// full round beat every partial one.  Tiles taller than 160 rows measured up
+// to 4% slower at 16384^2, beyond the on-package cache, and at most 1%
+// faster at 8192^2, so taller candidates are left out.
+constexpr double kOccupancyExponent = 0.7;
+constexpr long kMaxTileRows = 160;
 
 long march_tile_rows(long ny, long nstrips, int ts, int occupancy, long simds, long max_rows) {
     const long cap = max_rows < kMaxTileRows ? max_rows : kMaxTileRows;
@@ -547,14 +577,15 @@ long march_tile_rows(long ny, long nstrips, int ts, int occupancy, long simds, l
             best_rows = rows;
         }
     };
-    for (int w = 1; w <= occupancy; ++w) consider(w, kWaveEfficiency[w < 4 ? w : 4]);
+    for (int w = 1; w <= occupancy; ++w)
+        consider(w, std::pow((double)w / (double)occupancy, kOccupancyExponent));
     // Whole rounds: the fewest that bring the height under the cap (more
     // rounds only add halo rows).
     const long slots = (long)occupancy * simds;
     const long row_tiles_needed = (ny + cap - 1) / cap;
     long rounds = (row_tiles_needed * nstrips + slots - 1) / slots;
     if (rounds < 2) rounds = 2;
-    consider(rounds * occupancy, kWaveEfficiency[occupancy < 4 ? occupancy : 4]);
+    consider(rounds * occupancy, 1.0);
     return best_rows > 0 ? best_rows : cap;
 }
 
@@ -631,12 +662,12 @@ int launch_march_kv(const void *src, void *dst, const DiffPlan &p, double alpha,
                      ((uintptr_t)p.ld * sizeof(T)) % VB == 0;
     auto kernel = vec ? k_march<T, TS, KV, true, kLoadPolicy, kStorePolicy>
                       : k_march<T, TS, KV, false, kLoadPolicy, kStorePolicy>;
+    static SlotCache cache[2];
+    int per_cu = 0, cus = 0;
+    const int rc = resident_slots(reinterpret_cast<const void *>(kernel), cache[vec], &per_cu, &cus);
+    if (rc != SGC_OK) return rc;
     long rows = p.tile_rows;
     if (rows <= 0) {
-        static SlotCache cache[2];
-        int per_cu = 0, cus = 0;
-        const int rc = resident_slots(reinterpret_cast<const void *>(kernel), cache[vec], &per_cu, &cus);
-        if (rc != SGC_OK) return rc;
         const long model_rows = march_tile_rows(p.ny, g.nstrips, TS, per_cu, 4L * cus, max_rows);
         if (TS <= 2) {
             rows = 4;  // memory bound: many short tiles in flight
@@ -661,6 +692,7 @@ int launch_march_kv(const void *src, void *dst, const DiffPlan &p, double alpha,
     const long ntiles = (long)g.nstrips * ((p.ny + rows - 1) / rows);
     if (ntiles > 0x7fffffffL - 3) return fail(SGC_ERANGE, "too many tiles");
     g.ntiles = (int)ntiles;
+    g.balance = ntiles >= 2L * 4L * cus ? 1 : 0;
     const int blocks = (int)((ntiles + 3) / 4);
     hipLaunchKernelGGL(kernel, dim3(blocks), dim3(256), 0, s, g);
     return check_launch("diffusion march kernel");
