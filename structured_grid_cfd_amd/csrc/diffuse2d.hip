@@ -382,14 +382,18 @@ __device__ __forceinline__ bool march(const T *__restrict__ src, T *__restrict__
     // well ahead of the others and leaves the last one to run alone at a
     // fraction of the VALU rate for the end of the launch; with falling
     // priority, waves that are ahead yield to those behind and the waves of
-    // a SIMD finish close together.  A launch with fewer than two waves per
-    // SIMD has nothing to balance and keeps the default priority.
+    // a SIMD finish close together.  The host turns this off (`balance`) for
+    // the memory-bound shallow depths and for launches with fewer than two
+    // waves per SIMD, which keep the default priority.
     // One compare per iteration: `next` is the iteration of the next drop.
+    // Only depths of five and up ever balance; shallower marches compile
+    // without the check.
+    constexpr bool kBalanced = TS >= 5;
     int prio = 3;
-    int next = balance ? nit3 / 2 : INT_MAX;
-    if (balance) __builtin_amdgcn_s_setprio(3);
+    int next = (kBalanced && balance) ? nit3 / 2 : INT_MAX;
+    if (kBalanced && balance) __builtin_amdgcn_s_setprio(3);
     for (int it = 0; it < nit3; it += 3) {
-        if (it >= next) {
+        if (kBalanced && it >= next) {
             --prio;
             if (prio == 2) {
                 __builtin_amdgcn_s_setprio(2);
@@ -692,7 +696,10 @@ int launch_march_kv(const void *src, void *dst, const DiffPlan &p, double alpha,
     const long ntiles = (long)g.nstrips * ((p.ny + rows - 1) / rows);
     if (ntiles > 0x7fffffffL - 3) return fail(SGC_ERANGE, "too many tiles");
     g.ntiles = (int)ntiles;
-    g.balance = ntiles >= 2L * 4L * cus ? 1 : 0;
+    // Progress balancing pays where the march is bound by VALU issue (depth
+    // five and up) and the SIMDs hold two or more waves; the memory-bound
+    // shallow depths measured 5-13% slower with it.
+    g.balance = (TS >= 5 && ntiles >= 2L * 4L * cus) ? 1 : 0;
     const int blocks = (int)((ntiles + 3) / 4);
     hipLaunchKernelGGL(kernel, dim3(blocks), dim3(256), 0, s, g);
     return check_launch("diffusion march kernel");
