@@ -236,7 +236,8 @@ template <typename T, int KV> constexpr int march_out_width(int ts) {
 // it loads; the return value is true when that sum is not below `limit` (or is
 // NaN), in which case the stored results may differ from the separate form
 // and the caller recomputes the tile with FUSED off.
-template <typename T, int TS, int KV, bool VEC, bool EDGE, bool DOWN, int LPOL, int SPOL, bool FUSED>
+template <typename T, int TS, int KV, bool VEC, bool EDGE, bool DOWN, int LPOL, int SPOL, bool FUSED,
+          int EF = 0>
 __device__ __forceinline__ bool march(const T *__restrict__ src, T *__restrict__ dst, int nx,
                                       int ny, int ld, T a, T limit, int lane, int col_out0,
                                       int row_out0, int row_out1, bool balance) {
@@ -249,7 +250,17 @@ __device__ __forceinline__ bool march(const T *__restrict__ src, T *__restrict__
     const int c0 = col_out0 - HALO + lane * K;  // first column this lane holds
     bool colin[K];                              // column is an interior column
 #pragma unroll
-    for (int e = 0; e < K; ++e) colin[e] = EDGE ? (c0 + e >= 1 && c0 + e <= nx - 2) : true;
+    for (int e = 0; e < K; ++e) colin[e] = (EDGE || (EF & 1)) ? (c0 + e >= 1 && c0 + e <= nx - 2) : true;
+    // Fused form on the grid's edge (EF, with FUSED): bit 1, the strip holds
+    // column 0 or nx-1: loads of non-interior columns are masked to 0 and the
+    // two boundary columns take the coefficient 0 instead of alpha (c = 0 and
+    // t finite, which the overflow guard ensures, so c + 0*t is +0 exactly);
+    // columns beyond the boundary only ever feed the boundary column.  Bit 2,
+    // the tile reaches row 0 or ny-1: a level's row that is a boundary row or
+    // lies outside the grid is not computed but held at 0.
+    T ae[K];
+#pragma unroll
+    for (int e = 0; e < K; ++e) ae[e] = ((EF & 1) && (c0 + e == 0 || c0 + e == nx - 1)) ? T(0) : a;
 
     // DOWN marches from the top of the tile to its bottom (rows decreasing);
     // vertically adjacent tiles march in opposite directions so that the halo
@@ -275,7 +286,7 @@ __device__ __forceinline__ bool march(const T *__restrict__ src, T *__restrict__
 #pragma unroll
     for (int e = 0; e < K; ++e) {
         const int c = c0 + e;
-        st_off[e] = (c >= col_out0 && c < col_out0 + OW && (!EDGE || c < nx)) ? (uint32_t)c * ES : kOutOfRange;
+        st_off[e] = (c >= col_out0 && c < col_out0 + OW && c < nx) ? (uint32_t)c * ES : kOutOfRange;
     }
     uint32_t st_vec[KV];  // whole-vector stores (interior strips)
 #pragma unroll
@@ -308,7 +319,7 @@ __device__ __forceinline__ bool march(const T *__restrict__ src, T *__restrict__
             for (int e = 0; e < K; ++e)
                 x[e] = buf_load_elem<LPOL>((T *)nullptr, rin, roff + (uint32_t)(c0 + e) * ES);
         }
-        if (EDGE) {
+        if (EDGE || (EF & 1)) {
 #pragma unroll
             for (int e = 0; e < K; ++e) x[e] = colin[e] ? x[e] : T(0);
         }
@@ -338,7 +349,12 @@ __device__ __forceinline__ bool march(const T *__restrict__ src, T *__restrict__
         for (int e = 0; e < K; ++e) out[e] = T(0);
 #pragma unroll
         for (int s = 1; s <= TS; ++s) {
-            if (it >= 2 * s) {  // level s row r - DR*s depends only on loaded rows
+            if ((EF & 2) && it >= 2 * s && !(r - DR * s >= 1 && r - DR * s <= ny - 2)) {
+                if (s < TS) {
+#pragma unroll
+                    for (int e = 0; e < K; ++e) win[s < TS ? s : 0][P][e] = T(0);
+                }
+            } else if (it >= 2 * s) {  // level s row r - DR*s depends only on loaded rows
                 const int q = r - DR * s;
                 const bool rowin = !EDGE || (q >= 1 && q <= ny - 2);
                 const T wl = wave_shr1(win[s - 1][PC][K - 1]);
@@ -349,7 +365,7 @@ __device__ __forceinline__ bool march(const T *__restrict__ src, T *__restrict__
                     const T w = e == 0 ? wl : win[s - 1][PC][e - 1];
                     const T ee = e == K - 1 ? er : win[s - 1][PC][e + 1];
                     T val = FUSED ? five_point_fused(w, ee, win[s - 1][PSOUTH][e], win[s - 1][PNORTH][e],
-                                                     win[s - 1][PC][e], a)
+                                                     win[s - 1][PC][e], (EF & 1) ? ae[e] : a)
                                   : five_point(w, ee, win[s - 1][PSOUTH][e], win[s - 1][PNORTH][e],
                                                win[s - 1][PC][e], a);
                     if (EDGE) val = (colin[e] && rowin) ? val : T(0);
@@ -367,7 +383,7 @@ __device__ __forceinline__ bool march(const T *__restrict__ src, T *__restrict__
         // Row r - DR*TS of the last level; rows outside [row_out0, row_out1)
         // and discarded cells fall outside the store descriptor and are dropped.
         const uint32_t qoff = (uint32_t)(r - DR * TS - row_out0) * row_bytes;
-        if (VEC && !EDGE) {
+        if (VEC && !EDGE && !(EF & 1)) {
 #pragma unroll
             for (int v = 0; v < KV; ++v) buf_store_vec<SPOL, V>(out, v * V, rout, qoff + st_vec[v]);
         } else {
@@ -387,30 +403,55 @@ __device__ __forceinline__ bool march(const T *__restrict__ src, T *__restrict__
     // waves per SIMD, which keep the default priority.
     // One compare per iteration: `next` is the iteration of the next drop.
     // Only depths of five and up ever balance; shallower marches compile
-    // without the check.
+    // without the check.  Tiles on the grid's edge run the masked form, which
+    // costs more per row, so they start one level higher than interior tiles
+    // and keep it at every stage of their march: a SIMD holding an edge wave
+    // then serves it first, and its interior waves fill the gaps instead of
+    // finishing early while the edge wave runs on alone.
     constexpr bool kBalanced = TS >= 5;
-    int prio = 3;
+    constexpr int kTop = (EDGE || EF) ? 3 : 2;
+    int prio = kTop;
+    int stage = 0;
     int next = (kBalanced && balance) ? nit3 / 2 : INT_MAX;
-    if (kBalanced && balance) __builtin_amdgcn_s_setprio(3);
+    if (kBalanced && balance) __builtin_amdgcn_s_setprio(kTop);
     for (int it = 0; it < nit3; it += 3) {
         if (kBalanced && it >= next) {
-            --prio;
-            if (prio == 2) {
-                __builtin_amdgcn_s_setprio(2);
-                next = nit3 * 3 / 4;
-            } else if (prio == 1) {
-                __builtin_amdgcn_s_setprio(1);
-                next = nit3 * 7 / 8;
-            } else {
-                __builtin_amdgcn_s_setprio(0);
-                next = INT_MAX;
-            }
+            ++stage;
+            prio = prio > 0 ? prio - 1 : 0;
+            if (prio == 2) __builtin_amdgcn_s_setprio(2);
+            else if (prio == 1) __builtin_amdgcn_s_setprio(1);
+            else __builtin_amdgcn_s_setprio(0);
+            next = stage == 1 ? nit3 * 3 / 4 : (stage == 2 ? nit3 * 7 / 8 : INT_MAX);
         }
         step(std::integral_constant<int, 0>{}, it);
         step(std::integral_constant<int, 1>{}, it + 1);
         step(std::integral_constant<int, 2>{}, it + 2);
     }
     return FUSED && !(checksum < limit);
+}
+
+// One tile in the fused form, with the boundary handling its position needs
+// (EF above; edge tiles then cost about what interior tiles do, so no SIMD
+// holding one finishes late).  A wave whose inputs could push 4c past the
+// overflow threshold recomputes its tile in the separate form with per-cell
+// masks (same stores, now with the definition's bits).
+template <typename T, int TS, int KV, bool VEC, bool DOWN, int LPOL, int SPOL>
+__device__ __forceinline__ void march_tile(const T *src, T *dst, const MarchArgs &g, T a, T limit,
+                                           int lane, bool cols_in, bool rows_in, bool bal,
+                                           int col_out0, int row_out0, int row_out1) {
+    bool redo;
+    if (cols_in && rows_in)
+        redo = march<T, TS, KV, VEC, false, DOWN, LPOL, SPOL, true, 0>(
+            src, dst, g.nx, g.ny, g.ld, a, limit, lane, col_out0, row_out0, row_out1, bal);
+    else if (rows_in)
+        redo = march<T, TS, KV, VEC, false, DOWN, LPOL, SPOL, true, 1>(
+            src, dst, g.nx, g.ny, g.ld, a, limit, lane, col_out0, row_out0, row_out1, bal);
+    else
+        redo = march<T, TS, KV, VEC, false, DOWN, LPOL, SPOL, true, 3>(
+            src, dst, g.nx, g.ny, g.ld, a, limit, lane, col_out0, row_out0, row_out1, bal);
+    if (__any(redo))
+        march<T, TS, KV, VEC, true, DOWN, LPOL, SPOL, false>(src, dst, g.nx, g.ny, g.ld, a, limit, lane,
+                                                            col_out0, row_out0, row_out1, bal);
 }
 
 template <typename T, int TS, int KV, bool VEC, int LPOL, int SPOL>
@@ -436,36 +477,16 @@ __global__ __launch_bounds__(256) void k_march(MarchArgs g) {
     const int span0 = col_out0 - HALO;  // first column of the strip
     // Rows formed at any level lie within [row_out0 - TS - 2, row_out1 + TS + 1]
     // (the three-phase loop may run two rows past the last needed one).
-    const bool interior = span0 >= 1 && span0 + 64 * K <= g.nx - 1 && row_out0 - TS - 2 >= 1 &&
-                          row_out1 + TS + 2 <= g.ny - 2;
+    const bool cols_in = span0 >= 1 && span0 + 64 * K <= g.nx - 1;
+    const bool rows_in = row_out0 - TS - 2 >= 1 && row_out1 + TS + 2 <= g.ny - 2;
     const T limit = T(g.fuse_limit);
-    // Interior tiles take the fused form; a wave whose inputs could push 4c
-    // past the overflow threshold recomputes its tile in the separate form
-    // (same stores, now with the definition's bits).  Edge tiles always use
-    // the separate form.
-    if (rtile & 1) {
-        if (interior) {
-            const bool redo = march<T, TS, KV, VEC, false, true, LPOL, SPOL, true>(
-                src, dst, g.nx, g.ny, g.ld, a, limit, lane, col_out0, row_out0, row_out1, g.balance != 0);
-            if (__any(redo))
-                march<T, TS, KV, VEC, true, true, LPOL, SPOL, false>(
-                    src, dst, g.nx, g.ny, g.ld, a, limit, lane, col_out0, row_out0, row_out1, g.balance != 0);
-        } else {
-            march<T, TS, KV, VEC, true, true, LPOL, SPOL, false>(src, dst, g.nx, g.ny, g.ld, a, limit,
-                                                                 lane, col_out0, row_out0, row_out1, g.balance != 0);
-        }
-    } else {
-        if (interior) {
-            const bool redo = march<T, TS, KV, VEC, false, false, LPOL, SPOL, true>(
-                src, dst, g.nx, g.ny, g.ld, a, limit, lane, col_out0, row_out0, row_out1, g.balance != 0);
-            if (__any(redo))
-                march<T, TS, KV, VEC, true, false, LPOL, SPOL, false>(
-                    src, dst, g.nx, g.ny, g.ld, a, limit, lane, col_out0, row_out0, row_out1, g.balance != 0);
-        } else {
-            march<T, TS, KV, VEC, true, false, LPOL, SPOL, false>(src, dst, g.nx, g.ny, g.ld, a, limit,
-                                                                  lane, col_out0, row_out0, row_out1, g.balance != 0);
-        }
-    }
+    const bool bal = g.balance != 0;
+    if (rtile & 1)
+        march_tile<T, TS, KV, VEC, true, LPOL, SPOL>(src, dst, g, a, limit, lane, cols_in, rows_in, bal,
+                                                     col_out0, row_out0, row_out1);
+    else
+        march_tile<T, TS, KV, VEC, false, LPOL, SPOL>(src, dst, g, a, limit, lane, cols_in, rows_in, bal,
+                                                      col_out0, row_out0, row_out1);
 }
 
 // ---------------------------------------------------------------------------

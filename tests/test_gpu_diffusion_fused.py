@@ -1,11 +1,14 @@
-"""GPU parity of the marching sweep's interior tiles, which compute
-t - 4c through one fused multiply-add (the same rounding while 4c is finite)
-and fall back to the separate form when a tile's inputs are large enough for
-4c to overflow, or hold NaN or infinity.
+"""GPU parity of the marching sweep's fused form, which every tile takes: it
+computes t - 4c through one fused multiply-add (the same rounding while 4c is
+finite), holds the boundary columns at 0 through a zero coefficient and the
+boundary rows through skipped levels, and falls back to the separate form
+with per-cell masks when a tile's inputs are large enough for 4c to
+overflow, or hold NaN or infinity.
 
 Grids are large enough for many tiles away from every edge; magnitudes cover
 the ordinary range, values near the largest the fused form accepts, the
-subnormal range, and cells that force the fallback.  Every result is compared
+subnormal range, and cells that force the fallback, in an interior tile and
+in tiles on each edge and corner.  Every result is compared
 with the oracle bit for bit (NaN positions only, where inf - inf occurs).
 """
 import numpy as np
@@ -61,23 +64,30 @@ def test_extreme_magnitudes(dt, exp):
     _run(u, v, 16, 8, 16, f"2^{exp}")
 
 
+PLACES = {"interior": (NY // 2, NX // 2), "left": (NY // 2, 1), "right": (NY // 2, NX - 2),
+          "bottom": (1, NX // 3), "top": (NY - 2, NX // 3), "corner": (NY - 2, 1)}
+
+
 @pytest.mark.parametrize("dt", ["f64", "f32"])
 @pytest.mark.parametrize("kind", ["overflow", "nan", "inf"])
-def test_fallback_cells(dt, kind):
-    """A cell whose 4c overflows (centre 2**(emax-1), neighbours half that:
-    the separate form gives -inf where the fused one stays finite), a NaN, or
-    an infinity, placed in an interior tile: the tile must be recomputed in
-    the separate form."""
+@pytest.mark.parametrize("place", list(PLACES))
+def test_fallback_cells(dt, kind, place):
+    """A cell whose 4c overflows (centre 2**(emax-1), interior neighbours half
+    that: the separate form gives -inf where the fused one stays finite), a
+    NaN, or an infinity, placed in an interior tile or in a tile on an edge
+    or corner: the tile must be recomputed in the separate form."""
     u, v = inputs.uniform_grid(NX, NY, 73, DT[dt])
-    j, i = NY // 2, NX // 2
+    j, i = PLACES[place]
     big = np.ldexp(1.0, 1022 if dt == "f64" else 126)
     if kind == "overflow":
         u[j, i] = big
-        u[j, i - 1] = u[j, i + 1] = u[j - 1, i] = u[j + 1, i] = big / 2
+        for jj, ii in ((j, i - 1), (j, i + 1), (j - 1, i), (j + 1, i)):
+            if 1 <= jj <= NY - 2 and 1 <= ii <= NX - 2:
+                u[jj, ii] = big / 2
     elif kind == "nan":
         u[j, i] = np.nan
     else:
         u[j, i] = -np.inf
     for tb, rows in [(8, 16), (5, 0), (12, 24)]:
-        ref = _run(u, v, 2 * tb, tb, rows, f"fallback {kind}", nan_ok=True)
+        ref = _run(u, v, 2 * tb, tb, rows, f"fallback {kind} {place}", nan_ok=True)
         assert not np.isfinite(ref).all()
