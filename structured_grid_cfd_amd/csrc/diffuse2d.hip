@@ -403,13 +403,9 @@ __device__ __forceinline__ bool march(const T *__restrict__ src, T *__restrict__
     // waves per SIMD, which keep the default priority.
     // One compare per iteration: `next` is the iteration of the next drop.
     // Only depths of five and up ever balance; shallower marches compile
-    // without the check.  Tiles on the grid's edge run the masked form, which
-    // costs more per row, so they start one level higher than interior tiles
-    // and keep it at every stage of their march: a SIMD holding an edge wave
-    // then serves it first, and its interior waves fill the gaps instead of
-    // finishing early while the edge wave runs on alone.
+    // without the check.
     constexpr bool kBalanced = TS >= 5;
-    constexpr int kTop = (EDGE || EF) ? 3 : 2;
+    constexpr int kTop = 3;
     int prio = kTop;
     int stage = 0;
     int next = (kBalanced && balance) ? nit3 / 2 : INT_MAX;
