@@ -1,14 +1,19 @@
 """Launch settings of the production path: the maps, time block and tile
 shapes that the benchmark times and the full-size parity tests check."""
 
-# Five-point diffusion: temporal blocking, automatic tile rows.  Depth 10 on
-# grids of 4096^2 and up (whole-workload timings on MI355X, 1000 sweeps of
-# 4096^2 and 200 of 16384^2: FP64 depth 10 beat 8 by 2% and 11%, FP32 depth
-# 10 beat 8 and 12); depth 8 below, where each launch is latency bound and
-# the shallower march finishes sooner (9-20% faster at 128^2-2048^2).
+# Five-point diffusion: temporal blocking, automatic tile rows.  The depth
+# grows with the grid (whole-workload timings on MI355X, FP64): launches on
+# grids below 4096^2 take depth 8, large ones depth 10.
+#   below 2^24 cells: depth 8.  Small launches are latency bound (about 6 us
+#     each whatever the depth up to ~512^2), so depths 6-8 trade launch count
+#     against per-launch time and none wins everywhere (within 10% of each
+#     other at 64^2-1024^2, 32-840 sweeps); at 1280^2-3072^2 depth 8 is best
+#     or within 4%, and 5% ahead of 10 at 3072^2.
+#   from 2^24 cells (4096^2) up: depth 10 (4096^2 1000 sweeps: ahead of 8 by
+#     1-2% in FP64; 16384^2 FP32 200 sweeps: ahead of 8 and 12).
 DIFFUSION = {"map": "temporal", "time_block": 10, "tile_rows": 0}
 DIFFUSION_F32 = {"map": "temporal", "time_block": 10, "tile_rows": 0}
-SMALL_GRID_CELLS = 8 * 1024 * 1024  # below this, depth 8
+SMALL_GRID_CELLS = 1 << 24  # below this, depth 8
 
 # Per-variable field kernels.
 PACK = {"map": "tiled"}
