@@ -92,7 +92,15 @@ def host_cpu_model() -> str:
 
 
 def source_hash(path: Path) -> str:
-    return hashlib.sha256(path.read_bytes()).hexdigest()[:16]
+    """Hash of a source's code: lines with their // comments removed, blank
+    lines dropped, so that edits to comments alone keep recorded counters."""
+    code = []
+    for line in path.read_text().splitlines():
+        i = line.find("//")
+        line = (line[:i] if i >= 0 else line).rstrip()
+        if line:
+            code.append(line)
+    return hashlib.sha256("\n".join(code).encode()).hexdigest()[:16]
 
 
 def main():

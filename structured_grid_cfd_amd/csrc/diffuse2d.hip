@@ -227,15 +227,18 @@ template <typename T, int KV> constexpr int march_out_width(int ts) {
 }
 
 // One wave's march over output rows [row_out0, row_out1) and output columns
-// [col_out0, col_out0 + OW).  EDGE: some computed cell can lie on or outside
-// the grid boundary (first/last strip, first/last row tiles), so per-cell
-// row/column masks force those cells to 0; interior tiles skip every mask.
+// [col_out0, col_out0 + OW).
 // VEC: rows aligned to the lane vector, KV vector accesses per lane and row.
 // LPOL/SPOL: cache policy bits of the loads/stores (2 = non-temporal).
 // FUSED: cells use five_point_fused, and the lane adds up |x| over every value
 // it loads; the return value is true when that sum is not below `limit` (or is
 // NaN), in which case the stored results may differ from the separate form
 // and the caller recomputes the tile with FUSED off.
+// Boundary handling, for tiles some of whose computed cells lie on or outside
+// the grid's edge: EF (with FUSED) as described below; EDGE (the separate
+// form's fallback) forces every such cell to 0 with per-cell row/column masks.
+// Interior tiles take neither and run without masks.
+// balance: the wave lowers its issue priority as it progresses (below).
 template <typename T, int TS, int KV, bool VEC, bool EDGE, bool DOWN, int LPOL, int SPOL, bool FUSED,
           int EF = 0>
 __device__ __forceinline__ bool march(const T *__restrict__ src, T *__restrict__ dst, int nx,
