@@ -69,8 +69,8 @@ def parse():
                    help="sweeps of the CPU-baseline sample (same grid; 1000 = one full step, ~11 s)")
     p.add_argument("--kernels", default="all",
                    help="comma-separated sections of the per-kernel table: copy, diffusion "
-                        "(4096^2), small (64^2 and the size sweep), large (16384^2), pack, flux, "
-                        "2d (4800x1200 flux and packs), or all")
+                        "(4096^2), small (64^2 and the size sweep), fields (eight fields per call), "
+                        "large (16384^2), pack, flux, 2d (4800x1200 flux and packs), or all")
     p.add_argument("--ref-copy", action="store_true",
                    help="first run one 1 GiB copy (1 GiB read + 1 GiB written) as a known-size "
                         "reference for profiler byte counters")
@@ -378,6 +378,35 @@ def measure_all(log, sections=frozenset({"all"})) -> dict:
                 binding.stencil_diffuse2d_launches(100, cfg["map"], cfg["time_block"]),
                 {"time_block": cfg["time_block"]})
             del uu, vv
+
+    if want("fields"):
+        # eight fields of one grid: one multi-field call (shared launches)
+        # against eight single-field calls, 100 sweeps each, production depth
+        for n in (256, 1024):
+            cfg = launch_config.diffusion("f64", n, n)
+            pairs = [inputs.uniform_grid(n, n, 2100 + k, np.float64) for k in range(8)]
+            us = [dev(p0) for p0, _ in pairs]
+            vs = [dev(p1) for _, p1 in pairs]
+            L = binding.stencil_diffuse2d_launches(100, cfg["map"], cfg["time_block"])
+            work = 8 * (n - 2) ** 2 * 100
+            nbytes = 8 * (n * n + (n - 2) ** 2) * 8 * L
+
+            def multi():
+                binding.stencil_diffuse2d_fields(us, vs, n, 0.1, 100, cfg["map"], cfg["time_block"], 0,
+                                                 stream)
+
+            def separate():
+                for k in range(8):
+                    binding.stencil_diffuse2d(us[k], vs[k], n, 0.1, 100, cfg["map"], cfg["time_block"],
+                                              0, stream)
+
+            multi(); separate()
+            res[f"diffusion_fields_8x{n}_f64_100sweeps"] = entry(
+                timed(multi, 5, False), work, nbytes, {"time_block": cfg["time_block"], "launches": L})
+            res[f"diffusion_8_calls_{n}_f64_100sweeps"] = entry(
+                timed(separate, 5, False), work, nbytes, {"time_block": cfg["time_block"], "launches": 8 * L})
+            log("fields", n, res[f"diffusion_fields_8x{n}_f64_100sweeps"], res[f"diffusion_8_calls_{n}_f64_100sweeps"])
+            del us, vs
 
     if want("large"):
         # 16384^2 FP32, 200 sweeps

@@ -136,6 +136,30 @@ SGC_API int stencil_diffuse2d(void *u, void *v, int32_t dtype, int64_t nx, int64
                       int32_t *result_is_v);
 
 /*
+ * stencil_diffuse2d_fields -- the same sweeps applied to nvar independent
+ * fields of one shape in the same marching launches.  Field f is stepped
+ * exactly as stencil_diffuse2d(u[f], v[f], ...) would step it, bit for bit;
+ * the fields only share the launches (their tiles run side by side, so a
+ * small grid with several fields pays each launch's latency once).  [Mallard]
+ * "Design: single-GPU performance and parallel scaling", the reacting-flow
+ * changes: stencil kernels take all variables in one pass over the stencil;
+ * here all fields share each launch.
+ *
+ *   u, v        host arrays of nvar device buffers; each buffer as u / v of
+ *               stencil_diffuse2d (ld*ny elements of `dtype`).  No two of the
+ *               2*nvar buffers may overlap (SGC_EALIAS).
+ *   nvar        1 .. SGC_MAX_NVAR.
+ *   map         SGC_DIFF_TILED or SGC_DIFF_TEMPORAL (SGC_EINVAL otherwise).
+ *   the rest    as stencil_diffuse2d, for every field; the result is in
+ *               v[f] for every f if `steps` is odd, in u[f] if even.
+ * Errors are detected before anything is enqueued, as for stencil_diffuse2d.
+ */
+SGC_API int stencil_diffuse2d_fields(void *const *u, void *const *v, int32_t nvar, int32_t dtype,
+                                     int64_t nx, int64_t ny, int64_t ld, double alpha,
+                                     int64_t steps, int32_t map, int32_t time_block,
+                                     int32_t tile_rows, void *stream, int32_t *result_is_v);
+
+/*
  * stencil_diffuse2d_launches -- number of sweep-kernel launches a
  * stencil_diffuse2d call with these arguments enqueues (not counting the
  * one-off edge-ring initialisation of the interior-only page maps), or -1 if

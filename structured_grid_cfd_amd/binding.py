@@ -58,6 +58,9 @@ def load() -> ctypes.CDLL:
     lib.stencil_diffuse2d.argtypes = [vp, vp, i32, i64, i64, i64, dbl, i64, i32, i32, i32, vp,
                                       ctypes.POINTER(i32)]
     lib.stencil_diffuse2d.restype = ctypes.c_int
+    lib.stencil_diffuse2d_fields.argtypes = [vp, vp, i32, i32, i64, i64, i64, dbl, i64, i32, i32, i32,
+                                             vp, vp]
+    lib.stencil_diffuse2d_fields.restype = ctypes.c_int
     lib.stencil_diffuse2d_launches.argtypes = [i64, i32, i32]
     lib.stencil_diffuse2d_launches.restype = i64
     lib.field_pack.argtypes = [vp, i32, i64, i64, i64, i32, vp, i32, vp]
@@ -139,6 +142,26 @@ def stencil_diffuse2d(u: torch.Tensor, v: torch.Tensor, nx: int, alpha: float, s
     rc = load().stencil_diffuse2d(_dev_ptr(u), _dev_ptr(v), _dtype_code(u), nx, ny, ld,
                                   float(alpha), int(steps), m, int(time_block), int(tile_rows),
                                   _stream_ptr(stream), ctypes.byref(res))
+    _check(rc)
+    return bool(res.value)
+
+
+def stencil_diffuse2d_fields(us, vs, nx: int, alpha: float, steps: int, map: str | int = "temporal",
+                             time_block: int = 1, tile_rows: int = 0, stream=None) -> bool:
+    """The sweeps of :func:`stencil_diffuse2d` on several (ny, ld) pairs of one
+    shape and dtype in shared launches; returns True if every result is in its v."""
+    ul, vl = _as_list(us), _as_list(vs)
+    if not ul or len(ul) != len(vl):
+        raise ValueError("us and vs must be non-empty and of one length")
+    ny, ld = ul[0].shape
+    for t in ul + vl:
+        if t.dim() != 2 or tuple(t.shape) != (ny, ld) or t.dtype != ul[0].dtype:
+            raise ValueError("every field must be a 2D tensor of one shape and dtype")
+    m = DIFF_MAPS[map] if isinstance(map, str) else int(map)
+    res = ctypes.c_int32(-1)
+    rc = load().stencil_diffuse2d_fields(_table(ul), _table(vl), len(ul), _dtype_code(ul[0]), nx, ny,
+                                         ld, float(alpha), int(steps), m, int(time_block),
+                                         int(tile_rows), _stream_ptr(stream), ctypes.byref(res))
     _check(rc)
     return bool(res.value)
 

@@ -139,6 +139,33 @@ void flux_tables(const double *const *fx, const double *const *fy, const double 
     }
 }
 
+// The scalar arguments every diffusion entry point shares, with `fn` naming
+// the entry point in the messages.
+int check_diffusion_args(const char *fn, int32_t dtype, int64_t nx, int64_t ny, int64_t ld,
+                         double alpha, int64_t steps, int32_t map, int32_t time_block,
+                         int32_t tile_rows) {
+    const std::string f(fn);
+    if (dtype != SGC_F32 && dtype != SGC_F64)
+        return fail(SGC_EDTYPE, f + fmt(": unknown dtype %lld", dtype));
+    if (nx < 3 || ny < 3) return fail(SGC_EINVAL, f + ": nx and ny must be >= 3");
+    if (ld < nx) return fail(SGC_EINVAL, f + ": ld must be >= nx");
+    if (steps < 0) return fail(SGC_EINVAL, f + ": steps must be >= 0");
+    if (!std::isfinite(alpha)) return fail(SGC_EINVAL, f + ": alpha must be finite");
+    if (map < SGC_DIFF_COLLAPSE_BRANCH || map > SGC_DIFF_RESIDENT)
+        return fail(SGC_EINVAL, f + fmt(": unknown map %lld", map));
+    if (map == SGC_DIFF_TEMPORAL) {
+        if (time_block < 1) return fail(SGC_EINVAL, f + ": time_block must be >= 1");
+        if (time_block > SGC_MAX_TIME_BLOCK)
+            return fail(SGC_ERANGE, f + fmt(": time_block above %lld", SGC_MAX_TIME_BLOCK));
+    }
+    if (map == SGC_DIFF_TILED || map == SGC_DIFF_TEMPORAL) {
+        if (tile_rows < 0 || tile_rows > ny)
+            return fail(SGC_EINVAL, f + ": tile_rows must be 0 (auto) or 1..ny");
+    }
+    if (ld > kMaxElems / ny) return fail(SGC_ERANGE, f + ": ld*ny exceeds 2^31-1 elements");
+    return SGC_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -170,24 +197,9 @@ int stencil_diffuse2d(void *u, void *v, int32_t dtype, int64_t nx, int64_t ny, i
                       int32_t tile_rows, void *stream, int32_t *result_is_v) {
     clear();
     if (u == nullptr || v == nullptr) return fail(SGC_ENULL, "stencil_diffuse2d: u and v must be non-NULL");
-    if (dtype != SGC_F32 && dtype != SGC_F64)
-        return fail(SGC_EDTYPE, fmt("stencil_diffuse2d: unknown dtype %lld", dtype));
-    if (nx < 3 || ny < 3) return fail(SGC_EINVAL, "stencil_diffuse2d: nx and ny must be >= 3");
-    if (ld < nx) return fail(SGC_EINVAL, "stencil_diffuse2d: ld must be >= nx");
-    if (steps < 0) return fail(SGC_EINVAL, "stencil_diffuse2d: steps must be >= 0");
-    if (!std::isfinite(alpha)) return fail(SGC_EINVAL, "stencil_diffuse2d: alpha must be finite");
-    if (map < SGC_DIFF_COLLAPSE_BRANCH || map > SGC_DIFF_RESIDENT)
-        return fail(SGC_EINVAL, fmt("stencil_diffuse2d: unknown map %lld", map));
-    if (map == SGC_DIFF_TEMPORAL) {
-        if (time_block < 1) return fail(SGC_EINVAL, "stencil_diffuse2d: time_block must be >= 1");
-        if (time_block > SGC_MAX_TIME_BLOCK)
-            return fail(SGC_ERANGE, fmt("stencil_diffuse2d: time_block above %lld", SGC_MAX_TIME_BLOCK));
-    }
-    if (map == SGC_DIFF_TILED || map == SGC_DIFF_TEMPORAL) {
-        if (tile_rows < 0 || tile_rows > ny)
-            return fail(SGC_EINVAL, "stencil_diffuse2d: tile_rows must be 0 (auto) or 1..ny");
-    }
-    if (ld > kMaxElems / ny) return fail(SGC_ERANGE, "stencil_diffuse2d: ld*ny exceeds 2^31-1 elements");
+    int rc = check_diffusion_args("stencil_diffuse2d", dtype, nx, ny, ld, alpha, steps, map, time_block,
+                                  tile_rows);
+    if (rc) return rc;
     const int64_t es = dtype == SGC_F64 ? 8 : 4;
     const int64_t bytes = ld * ny * es;
     if (misaligned(u, es) || misaligned(v, es))
@@ -196,7 +208,6 @@ int stencil_diffuse2d(void *u, void *v, int32_t dtype, int64_t nx, int64_t ny, i
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     DiffPlan p{(int)nx, (int)ny, (int)ld, time_block, tile_rows};
-    int rc = SGC_OK;
     if (steps == 0) {
         rc = diffuse_zero_ring(u, dtype, p.nx, p.ny, p.ld, s);
         if (rc) return rc;
@@ -230,6 +241,68 @@ int stencil_diffuse2d(void *u, void *v, int32_t dtype, int64_t nx, int64_t ny, i
             const bool fwd = (k & 1) == 0;
             rc = diffuse_sweep(fwd ? u : v, fwd ? v : u, dtype, p, alpha, map, ts, s);
             if (rc) return rc;
+        }
+    }
+    if (result_is_v) *result_is_v = (int32_t)(steps & 1);
+    return SGC_OK;
+}
+
+int stencil_diffuse2d_fields(void *const *u, void *const *v, int32_t nvar, int32_t dtype, int64_t nx,
+                             int64_t ny, int64_t ld, double alpha, int64_t steps, int32_t map,
+                             int32_t time_block, int32_t tile_rows, void *stream,
+                             int32_t *result_is_v) {
+    clear();
+    const char *fn = "stencil_diffuse2d_fields";
+    if (u == nullptr || v == nullptr)
+        return fail(SGC_ENULL, "stencil_diffuse2d_fields: the u and v tables must be non-NULL");
+    if (nvar < 1 || nvar > SGC_MAX_NVAR)
+        return fail(SGC_EINVAL, fmt("stencil_diffuse2d_fields: nvar must be 1..%lld", SGC_MAX_NVAR));
+    int rc = check_diffusion_args(fn, dtype, nx, ny, ld, alpha, steps, map, time_block, tile_rows);
+    if (rc) return rc;
+    if (map != SGC_DIFF_TILED && map != SGC_DIFF_TEMPORAL)
+        return fail(SGC_EINVAL, "stencil_diffuse2d_fields: map must be SGC_DIFF_TILED or SGC_DIFF_TEMPORAL");
+    const int64_t es = dtype == SGC_F64 ? 8 : 4;
+    const int64_t bytes = ld * ny * es;
+    for (int32_t k = 0; k < nvar; ++k) {
+        if (u[k] == nullptr || v[k] == nullptr)
+            return fail(SGC_ENULL, fmt("stencil_diffuse2d_fields: u or v entry %lld is NULL", k));
+        if (misaligned(u[k], es) || misaligned(v[k], es))
+            return fail(SGC_EINVAL, fmt("stencil_diffuse2d_fields: field %lld is not aligned to its element size", k));
+    }
+    // No two of the 2*nvar buffers may overlap.
+    for (int32_t a = 0; a < 2 * nvar; ++a) {
+        const void *pa = a < nvar ? u[a] : v[a - nvar];
+        for (int32_t b = a + 1; b < 2 * nvar; ++b) {
+            const void *pb = b < nvar ? u[b] : v[b - nvar];
+            if (overlaps(pa, bytes, pb, bytes))
+                return fail(SGC_EALIAS, fmt("stencil_diffuse2d_fields: buffer %lld", a) + fmt(" overlaps buffer %lld (u entries first, then v)", b));
+        }
+    }
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    DiffPlan p{(int)nx, (int)ny, (int)ld, time_block, tile_rows};
+    FieldPairs fwd{}, back{};
+    fwd.n = back.n = nvar;
+    for (int32_t k = 0; k < nvar; ++k) {
+        fwd.src[k] = u[k];
+        fwd.dst[k] = v[k];
+        back.src[k] = v[k];
+        back.dst[k] = u[k];
+    }
+    if (steps == 0) {
+        for (int32_t k = 0; k < nvar; ++k)
+            if ((rc = diffuse_zero_ring(u[k], dtype, p.nx, p.ny, p.ld, s))) return rc;
+    } else if (map == SGC_DIFF_TILED) {
+        // The march treats the ring as 0 on read and writes it as 0.
+        for (int64_t k = 1; k <= steps; ++k)
+            if ((rc = diffuse_sweep_fields((k & 1) ? fwd : back, dtype, p, alpha, map, 1, s))) return rc;
+    } else {  // TEMPORAL: the single-field launch schedule
+        const int64_t L = temporal_launches(steps, time_block);
+        const int64_t base = steps / L, extra = steps % L;
+        for (int64_t k = 0; k < L; ++k) {
+            const int ts = (int)(base + (k < extra ? 1 : 0));
+            if ((rc = diffuse_sweep_fields((k & 1) == 0 ? fwd : back, dtype, p, alpha, map, ts, s)))
+                return rc;
         }
     }
     if (result_is_v) *result_is_v = (int32_t)(steps & 1);

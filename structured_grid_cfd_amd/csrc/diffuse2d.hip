@@ -205,11 +205,12 @@ __device__ __forceinline__ void buf_store_elem(double x, __amdgpu_buffer_rsrc_t 
 }
 
 struct MarchArgs {
-    const void *src;
-    void *dst;
+    const void *src[SGC_MAX_NVAR];  // per field
+    void *dst[SGC_MAX_NVAR];
     int nx, ny, ld;
-    int nstrips;    // strips across the grid (OW output columns each)
-    int ntiles;     // nstrips * row tiles
+    int nstrips;      // strips across the grid (OW output columns each)
+    int field_tiles;  // nstrips * row tiles: the tiles of one field
+    int ntiles;       // fields * field_tiles; tile t is field t / field_tiles
     int tile_rows;  // output rows per tile
     double alpha;
     double fuse_limit;  // fused form allowed while sum |input| stays below this
@@ -465,13 +466,15 @@ __global__ __launch_bounds__(256) void k_march(MarchArgs g) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int tile = xcd_remap(blockIdx.x, gridDim.x) * 4 + wave;
     if (tile >= g.ntiles) return;  // whole wave leaves; the kernel has no barriers
-    const int strip = tile % g.nstrips;
-    const int rtile = tile / g.nstrips;
+    const int field = tile / g.field_tiles;
+    const int ftile = tile - field * g.field_tiles;
+    const int strip = ftile % g.nstrips;
+    const int rtile = ftile / g.nstrips;
     const int col_out0 = strip * OW;
     const int row_out0 = rtile * g.tile_rows;
     const int row_out1 = min(row_out0 + g.tile_rows, g.ny);
-    const T *src = static_cast<const T *>(g.src);
-    T *dst = static_cast<T *>(g.dst);
+    const T *src = static_cast<const T *>(g.src[field]);
+    T *dst = static_cast<T *>(g.dst[field]);
     const T a = T(g.alpha);
     const int span0 = col_out0 - HALO;  // first column of the strip
     // Rows formed at any level lie within [row_out0 - TS - 2, row_out1 + TS + 1]
@@ -662,10 +665,12 @@ template <typename T> double march_fuse_limit(double alpha, int ts) {
 }
 
 template <typename T, int TS, int KV>
-int launch_march_kv(const void *src, void *dst, const DiffPlan &p, double alpha, hipStream_t s) {
-    MarchArgs g;
-    g.src = src;
-    g.dst = dst;
+int launch_march_kv(const FieldPairs &f, const DiffPlan &p, double alpha, hipStream_t s) {
+    MarchArgs g{};
+    for (int k = 0; k < f.n; ++k) {
+        g.src[k] = f.src[k];
+        g.dst[k] = f.dst[k];
+    }
     g.nx = p.nx;
     g.ny = p.ny;
     g.ld = p.ld;
@@ -673,6 +678,8 @@ int launch_march_kv(const void *src, void *dst, const DiffPlan &p, double alpha,
     g.fuse_limit = march_fuse_limit<T>(alpha, TS);
     const int ow = march_out_width<T, KV>(TS);
     g.nstrips = (p.nx + ow - 1) / ow;
+    // Strips of all fields: the tile model sees the fields side by side.
+    const long strips_all = (long)g.nstrips * f.n;
     // Keep every descriptor within 2^30 bytes and every offset a wave can
     // form (its rows plus the halo and prefetch rows around them) below
     // 2^30, so that offsets outside a wave's rows, and the out-of-range
@@ -681,9 +688,10 @@ int launch_march_kv(const void *src, void *dst, const DiffPlan &p, double alpha,
     const long max_rows = (1L << 30) / row_bytes - 2 * TS - 8;
     if (max_rows < 1) return fail(SGC_ERANGE, "grid rows too wide for the marching sweep");
     constexpr uintptr_t VB = sizeof(T) * lane_elems<T>(TS);
-    const bool vec = (reinterpret_cast<uintptr_t>(src) % VB == 0) &&
-                     (reinterpret_cast<uintptr_t>(dst) % VB == 0) &&
-                     ((uintptr_t)p.ld * sizeof(T)) % VB == 0;
+    bool vec = ((uintptr_t)p.ld * sizeof(T)) % VB == 0;
+    for (int k = 0; k < f.n; ++k)
+        vec = vec && reinterpret_cast<uintptr_t>(f.src[k]) % VB == 0 &&
+              reinterpret_cast<uintptr_t>(f.dst[k]) % VB == 0;
     auto kernel = vec ? k_march<T, TS, KV, true, kLoadPolicy, kStorePolicy>
                       : k_march<T, TS, KV, false, kLoadPolicy, kStorePolicy>;
     static SlotCache cache[2];
@@ -692,14 +700,14 @@ int launch_march_kv(const void *src, void *dst, const DiffPlan &p, double alpha,
     if (rc != SGC_OK) return rc;
     long rows = p.tile_rows;
     if (rows <= 0) {
-        const long model_rows = march_tile_rows(p.ny, g.nstrips, TS, per_cu, 4L * cus, max_rows);
+        const long model_rows = march_tile_rows(p.ny, strips_all, TS, per_cu, 4L * cus, max_rows);
         if (TS <= 2) {
             rows = 4;  // memory bound: many short tiles in flight
         } else if (TS == 3) {
             rows = 8;
         } else if (TS == 4) {
             // Between memory and ALU bound: about 8192 tiles of 16 to 128 rows.
-            rows = max(16L, min((long)p.ny * g.nstrips / 8192, 128L));
+            rows = max(16L, min((long)p.ny * strips_all / 8192, 128L));
         } else {
             rows = model_rows;
         }
@@ -707,14 +715,16 @@ int launch_march_kv(const void *src, void *dst, const DiffPlan &p, double alpha,
         // heights is latency bound: each launch lasts as long as one wave's
         // march, so it takes the model's height (the shortest tiles that
         // spread the grid over the resident waves) instead.
-        const long tiles = (long)g.nstrips * ((p.ny + rows - 1) / rows);
+        const long tiles = strips_all * ((p.ny + rows - 1) / rows);
         if (TS <= 4 && tiles < (long)per_cu * 4L * cus) rows = min(rows, model_rows);
     }
     rows = min(rows, (long)p.ny);
     rows = min(rows, max_rows);
     g.tile_rows = (int)rows;
-    const long ntiles = (long)g.nstrips * ((p.ny + rows - 1) / rows);
+    const long field_tiles = (long)g.nstrips * ((p.ny + rows - 1) / rows);
+    const long ntiles = field_tiles * f.n;
     if (ntiles > 0x7fffffffL - 3) return fail(SGC_ERANGE, "too many tiles");
+    g.field_tiles = (int)field_tiles;
     g.ntiles = (int)ntiles;
     // Progress balancing pays where the march is bound by VALU issue (depth
     // five and up) and the SIMDs hold two or more waves; the memory-bound
@@ -726,16 +736,15 @@ int launch_march_kv(const void *src, void *dst, const DiffPlan &p, double alpha,
 }
 
 template <typename T, int TS>
-int launch_march_ts(const void *src, void *dst, const DiffPlan &p, double alpha, hipStream_t s) {
-    return launch_march_kv<T, TS, vectors_per_lane<T>(TS)>(src, dst, p, alpha, s);
+int launch_march_ts(const FieldPairs &f, const DiffPlan &p, double alpha, hipStream_t s) {
+    return launch_march_kv<T, TS, vectors_per_lane<T>(TS)>(f, p, alpha, s);
 }
 
 template <typename T>
-int launch_march(const void *src, void *dst, const DiffPlan &p, double alpha, int ts,
-                 hipStream_t s) {
+int launch_march(const FieldPairs &f, const DiffPlan &p, double alpha, int ts, hipStream_t s) {
     switch (ts) {
 #define SGC_TS_CASE(n) \
-    case n: return launch_march_ts<T, n>(src, dst, p, alpha, s);
+    case n: return launch_march_ts<T, n>(f, p, alpha, s);
         SGC_TS_CASE(1) SGC_TS_CASE(2) SGC_TS_CASE(3) SGC_TS_CASE(4)
         SGC_TS_CASE(5) SGC_TS_CASE(6) SGC_TS_CASE(7) SGC_TS_CASE(8)
         SGC_TS_CASE(9) SGC_TS_CASE(10) SGC_TS_CASE(11) SGC_TS_CASE(12)
@@ -765,9 +774,13 @@ int sweep_t(const void *src, void *dst, const DiffPlan &p, double alpha, int map
         hipLaunchKernelGGL((k_strided<T>), dim3(p.nx - 2), dim3(256), 0, s, in, out, p.nx, p.ny, p.ld, a);
         return check_launch("strided-lane sweep");
     case SGC_DIFF_TILED:
-        return launch_march<T>(src, dst, p, alpha, 1, s);
-    case SGC_DIFF_TEMPORAL:
-        return launch_march<T>(src, dst, p, alpha, ts, s);
+    case SGC_DIFF_TEMPORAL: {
+        FieldPairs f{};
+        f.src[0] = src;
+        f.dst[0] = dst;
+        f.n = 1;
+        return launch_march<T>(f, p, alpha, map == SGC_DIFF_TILED ? 1 : ts, s);
+    }
     default:
         return fail(SGC_EINVAL, "unknown diffusion map");
     }
@@ -813,6 +826,16 @@ int diffuse_sweep(const void *src, void *dst, int dtype, const DiffPlan &p, doub
                   int steps_in_launch, hipStream_t s) {
     if (dtype == SGC_F64) return sweep_t<double>(src, dst, p, alpha, map, steps_in_launch, s);
     return sweep_t<float>(src, dst, p, alpha, map, steps_in_launch, s);
+}
+
+int diffuse_sweep_fields(const FieldPairs &f, int dtype, const DiffPlan &p, double alpha, int map,
+                         int steps_in_launch, hipStream_t s) {
+    if (f.n < 1 || f.n > SGC_MAX_NVAR) return fail(SGC_EINVAL, "field count out of range");
+    if (map != SGC_DIFF_TILED && map != SGC_DIFF_TEMPORAL)
+        return fail(SGC_EINVAL, "several fields per launch need the TILED or TEMPORAL map");
+    const int ts = map == SGC_DIFF_TILED ? 1 : steps_in_launch;
+    if (dtype == SGC_F64) return launch_march<double>(f, p, alpha, ts, s);
+    return launch_march<float>(f, p, alpha, ts, s);
 }
 
 }  // namespace sgc

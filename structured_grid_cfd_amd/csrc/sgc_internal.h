@@ -65,6 +65,15 @@ int diffuse_resident(const void *src, void *dst, void *prev, int dtype, const Di
                      double alpha, int steps, hipStream_t s);
 int diffuse_sweep(const void *src, void *dst, int dtype, const DiffPlan &p,
                   double alpha, int map, int steps_in_launch, hipStream_t s);
+// Several fields of the same shape stepped in the same marching launches
+// (maps TILED and TEMPORAL): field f reads src[f] and writes dst[f].
+struct FieldPairs {
+    const void *src[SGC_MAX_NVAR];
+    void *dst[SGC_MAX_NVAR];
+    int n;
+};
+int diffuse_sweep_fields(const FieldPairs &f, int dtype, const DiffPlan &p, double alpha, int map,
+                         int steps_in_launch, hipStream_t s);
 
 // ---- per-variable field kernels (field_pack.hip, flux_diff.hip) ------------
 struct PtrTable {

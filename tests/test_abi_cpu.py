@@ -9,7 +9,7 @@ import pytest
 
 from structured_grid_cfd_amd import binding as b
 
-EXPECTED = ["stencil_diffuse2d", "stencil_diffuse2d_launches", "field_pack", "field_unpack",
+EXPECTED = ["stencil_diffuse2d", "stencil_diffuse2d_fields", "stencil_diffuse2d_launches", "field_pack", "field_unpack",
             "flux_diff3d", "flux_stage3d", "sgc_last_error", "sgc_abi_version"]
 
 
@@ -160,6 +160,30 @@ def test_stage_validation(lib):
     assert call(_tab(V + 0x1000 + 8)) == 4                 # qout straddles q
     assert call(_tab(V + 4)) == 1                          # misaligned
     assert call(_tab(V + 0x3000), n=(3000, 3000, 3000)) == 5
+
+
+def test_fields_validation(lib):
+    """stencil_diffuse2d_fields: every field's pointers and every pair of the
+    2*nvar buffers are checked, and only the marching maps are accepted."""
+    u, v = _tab(U, U + 0x1000), _tab(V, V + 0x1000)
+    base = (1, 8, 8, 8, 0.1, 1, 4, 2, 0)  # f64, nx, ny, ld, alpha, steps, TEMPORAL, time_block, rows
+
+    def call(uu, vv, n, *rest):
+        return lib.stencil_diffuse2d_fields(uu, vv, n, *rest, None, None)
+
+    assert call(None, v, 2, *base) == 2 and "non-NULL" in b.last_error()
+    assert call(u, v, 0, *base) == 1 and "nvar" in b.last_error()
+    assert call(u, v, 33, *base) == 1 and "nvar" in b.last_error()
+    assert call(u, v, 2, 7, 8, 8, 8, 0.1, 1, 4, 2, 0) == 3                     # dtype
+    assert call(u, v, 2, 1, 8, 8, 7, 0.1, 1, 4, 2, 0) == 1                     # ld < nx
+    assert call(u, v, 2, 1, 8, 8, 8, 0.1, 1, 4, 13, 0) == 5                    # time_block
+    for m in (0, 1, 2, 5):                                                     # page maps, resident
+        assert call(u, v, 2, 1, 8, 8, 8, 0.1, 1, m, 1, 0) == 1 and "map" in b.last_error()
+    assert call(_tab(U, 0), v, 2, *base) == 2 and "entry 1" in b.last_error()
+    assert call(_tab(U, U + 0x1004), v, 2, *base) == 1 and "aligned" in b.last_error()
+    assert call(_tab(U, U + 8 * 63), v, 2, *base) == 4 and "overlap" in b.last_error()  # u[0], u[1]
+    assert call(u, _tab(V, U + 8 * 7), 2, *base) == 4                          # v[1] on u[0]
+    assert call(u, _tab(V, V), 2, *base) == 4                                  # v[0] is v[1]
 
 
 def test_last_error_is_per_call(lib):
