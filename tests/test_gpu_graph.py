@@ -74,6 +74,34 @@ def test_diffusion_graph_replays(dt, m, tb, off, steps):
     _replays(g, reset, lambda: v if in_v else u, ref, f"diffusion {m}")
 
 
+def test_fields_graph_replays():
+    """Three fields stepped in shared launches, captured once and replayed."""
+    nx, ny = 300, 170
+    pairs = [inputs.uniform_grid(nx, ny, 1310 + k, np.float64) for k in range(3)]
+    us = [torch.zeros(ny, nx, dtype=torch.float64, device="cuda") for _ in pairs]
+    vs = [torch.zeros_like(t) for t in us]
+    say("graph fields")
+
+    def reset():
+        for t, (a, b_) in zip(us + vs, [(a, None) for a, _ in pairs] + [(b_, None) for _, b_ in pairs]):
+            t.copy_(torch.from_numpy(a))
+
+    reset()
+    g = _capture(lambda: binding.stencil_diffuse2d_fields(us, vs, nx, 0.1, 23, "temporal", 10))
+    reset()
+    in_v = binding.stencil_diffuse2d_fields(us, vs, nx, 0.1, 23, "temporal", 10)
+    torch.cuda.synchronize()
+    refs = [host(v if in_v else u).copy() for u, v in zip(us, vs)]
+    for rep in range(3):
+        reset()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, (u, v) in enumerate(zip(us, vs)):
+            assert_bitwise(host(v if in_v else u), refs[k], f"fields replay {rep} field {k}")
+        _ = (torch.ones(1 << 20, device="cuda") * rep).sum().item()
+
+
 def test_pack_flux_and_stage_graph_replays():
     f = inputs.normal_fields(4, 67, 45, 23, 1302)
     fi = inputs.normal_faces(4, 67, 45, 23, 1303)
