@@ -407,6 +407,28 @@ def measure_all(log, sections=frozenset({"all"})) -> dict:
                 timed(separate, 5, False), work, nbytes, {"time_block": cfg["time_block"], "launches": 8 * L})
             log("fields", n, res[f"diffusion_fields_8x{n}_f64_100sweeps"], res[f"diffusion_8_calls_{n}_f64_100sweeps"])
             del us, vs
+        # eight 64^2 fields, 32 sweeps, resident map: one workgroup per field
+        c = inputs.cfg1()
+        us = [dev(c["u"]) for _ in range(8)]
+        vs = [dev(c["v"]) for _ in range(8)]
+        work = 8 * 62 * 62 * 32
+        nbytes = 8 * (64 * 64 + 62 * 62) * 8
+
+        def rmulti():
+            binding.stencil_diffuse2d_fields(us, vs, 64, 0.1, 32, "resident", 1, 0, stream)
+
+        def rseparate():
+            for k in range(8):
+                binding.stencil_diffuse2d(us[k], vs[k], 64, 0.1, 32, "resident", 1, 0, stream)
+
+        rmulti(); rseparate()
+        res["diffusion_fields_8x64_f64_32sweeps_resident"] = entry(timed(rmulti, 10, False), work, nbytes,
+                                                                   {"map": "resident", "launches": 1})
+        res["diffusion_8_calls_64_f64_32sweeps_resident"] = entry(timed(rseparate, 10, False), work, nbytes,
+                                                                  {"map": "resident", "launches": 8})
+        log("fields resident", res["diffusion_fields_8x64_f64_32sweeps_resident"],
+            res["diffusion_8_calls_64_f64_32sweeps_resident"])
+        del us, vs
 
     if want("large"):
         # 16384^2 FP32, 200 sweeps

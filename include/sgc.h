@@ -149,7 +149,10 @@ SGC_API int stencil_diffuse2d(void *u, void *v, int32_t dtype, int64_t nx, int64
  *               stencil_diffuse2d (ld*ny elements of `dtype`).  No two of the
  *               2*nvar buffers may overlap (SGC_EALIAS).
  *   nvar        1 .. SGC_MAX_NVAR.
- *   map         SGC_DIFF_TILED or SGC_DIFF_TEMPORAL (SGC_EINVAL otherwise).
+ *   map         SGC_DIFF_TILED, SGC_DIFF_TEMPORAL or SGC_DIFF_RESIDENT
+ *               (SGC_EINVAL otherwise); RESIDENT runs one workgroup per field
+ *               with stencil_diffuse2d's limits (SGC_ERANGE beyond them) and
+ *               leaves each field's state one step earlier in its other buffer.
  *   the rest    as stencil_diffuse2d, for every field; the result is in
  *               v[f] for every f if `steps` is odd, in u[f] if even.
  * Errors are detected before anything is enqueued, as for stencil_diffuse2d.

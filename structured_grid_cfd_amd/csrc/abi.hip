@@ -259,8 +259,13 @@ int stencil_diffuse2d_fields(void *const *u, void *const *v, int32_t nvar, int32
         return fail(SGC_EINVAL, fmt("stencil_diffuse2d_fields: nvar must be 1..%lld", SGC_MAX_NVAR));
     int rc = check_diffusion_args(fn, dtype, nx, ny, ld, alpha, steps, map, time_block, tile_rows);
     if (rc) return rc;
-    if (map != SGC_DIFF_TILED && map != SGC_DIFF_TEMPORAL)
-        return fail(SGC_EINVAL, "stencil_diffuse2d_fields: map must be SGC_DIFF_TILED or SGC_DIFF_TEMPORAL");
+    if (map != SGC_DIFF_TILED && map != SGC_DIFF_TEMPORAL && map != SGC_DIFF_RESIDENT)
+        return fail(SGC_EINVAL,
+                    "stencil_diffuse2d_fields: map must be SGC_DIFF_TILED, SGC_DIFF_TEMPORAL or SGC_DIFF_RESIDENT");
+    if (map == SGC_DIFF_RESIDENT && (nx > 64 || ny > 128))
+        return fail(SGC_ERANGE, "stencil_diffuse2d_fields: the resident map takes grids of at most 64 columns and 128 rows");
+    if (map == SGC_DIFF_RESIDENT && steps > 0x7fffffffLL)
+        return fail(SGC_ERANGE, "stencil_diffuse2d_fields: the resident map takes at most 2^31-1 steps");
     const int64_t es = dtype == SGC_F64 ? 8 : 4;
     const int64_t bytes = ld * ny * es;
     for (int32_t k = 0; k < nvar; ++k) {
@@ -292,6 +297,17 @@ int stencil_diffuse2d_fields(void *const *u, void *const *v, int32_t nvar, int32
     if (steps == 0) {
         for (int32_t k = 0; k < nvar; ++k)
             if ((rc = diffuse_zero_ring(u[k], dtype, p.nx, p.ny, p.ld, s))) return rc;
+    } else if (map == SGC_DIFF_RESIDENT) {
+        // One workgroup per field, every step in one launch; the other buffer
+        // ends with the state one step earlier, as for a single field.
+        const bool odd = (steps & 1) != 0;
+        ResidentFields r{};
+        for (int32_t k = 0; k < nvar; ++k) {
+            r.src[k] = u[k];
+            r.dst[k] = odd ? v[k] : u[k];
+            r.prev[k] = odd ? u[k] : v[k];
+        }
+        if ((rc = diffuse_resident_fields(r, nvar, dtype, p, alpha, (int)steps, s))) return rc;
     } else if (map == SGC_DIFF_TILED) {
         // The march treats the ring as 0 on read and writes it as 0.
         for (int64_t k = 1; k <= steps; ++k)

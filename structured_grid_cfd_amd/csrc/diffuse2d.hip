@@ -511,8 +511,12 @@ constexpr int kResidentWaves = 16;
 constexpr int kResidentCols = 64;
 
 template <typename T, int R>
-__global__ __launch_bounds__(1024) void k_resident(const T *src, T *dst, T *prev, int nx, int ny,
-                                                   int ld, T a, int steps) {
+__global__ __launch_bounds__(1024) void k_resident(ResidentFields f, int nx, int ny, int ld, T a,
+                                                   int steps) {
+    // One workgroup per field.
+    const T *src = static_cast<const T *>(f.src[blockIdx.x]);
+    T *dst = static_cast<T *>(f.dst[blockIdx.x]);
+    T *prev = static_cast<T *>(f.prev[blockIdx.x]);
     __shared__ T edge[2][kResidentWaves][2][kResidentCols];  // [slot set][wave][first, last row][lane]
     const int i = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
@@ -801,25 +805,32 @@ int diffuse_zero_ring(void *buf, int dtype, int nx, int ny, int ld, hipStream_t 
 }
 
 template <typename T>
-int resident_t(const void *src, void *dst, void *prev, const DiffPlan &p, double alpha, int steps,
+int resident_t(const ResidentFields &f, int n, const DiffPlan &p, double alpha, int steps,
                hipStream_t s) {
-    const T *in = static_cast<const T *>(src);
-    T *out = static_cast<T *>(dst);
-    T *before = static_cast<T *>(prev);
     const T a = T(alpha);
     if (p.ny <= kResidentWaves * 4)
-        hipLaunchKernelGGL((k_resident<T, 4>), dim3(1), dim3(1024), 0, s, in, out, before, p.nx, p.ny, p.ld, a, steps);
+        hipLaunchKernelGGL((k_resident<T, 4>), dim3(n), dim3(1024), 0, s, f, p.nx, p.ny, p.ld, a, steps);
     else
-        hipLaunchKernelGGL((k_resident<T, 8>), dim3(1), dim3(1024), 0, s, in, out, before, p.nx, p.ny, p.ld, a, steps);
+        hipLaunchKernelGGL((k_resident<T, 8>), dim3(n), dim3(1024), 0, s, f, p.nx, p.ny, p.ld, a, steps);
     return check_launch("diffusion resident sweep");
+}
+
+int diffuse_resident_fields(const ResidentFields &f, int n, int dtype, const DiffPlan &p,
+                            double alpha, int steps, hipStream_t s) {
+    if (p.nx > kResidentCols || p.ny > kResidentWaves * 8)
+        return fail(SGC_ERANGE, "resident sweep: the grid must fit 64 columns and 128 rows");
+    if (n < 1 || n > SGC_MAX_NVAR) return fail(SGC_EINVAL, "field count out of range");
+    if (dtype == SGC_F64) return resident_t<double>(f, n, p, alpha, steps, s);
+    return resident_t<float>(f, n, p, alpha, steps, s);
 }
 
 int diffuse_resident(const void *src, void *dst, void *prev, int dtype, const DiffPlan &p, double alpha,
                      int steps, hipStream_t s) {
-    if (p.nx > kResidentCols || p.ny > kResidentWaves * 8)
-        return fail(SGC_ERANGE, "resident sweep: the grid must fit 64 columns and 128 rows");
-    if (dtype == SGC_F64) return resident_t<double>(src, dst, prev, p, alpha, steps, s);
-    return resident_t<float>(src, dst, prev, p, alpha, steps, s);
+    ResidentFields f{};
+    f.src[0] = src;
+    f.dst[0] = dst;
+    f.prev[0] = prev;
+    return diffuse_resident_fields(f, 1, dtype, p, alpha, steps, s);
 }
 
 int diffuse_sweep(const void *src, void *dst, int dtype, const DiffPlan &p, double alpha, int map,

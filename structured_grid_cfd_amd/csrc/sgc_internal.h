@@ -63,6 +63,14 @@ int diffuse_zero_ring(void *buf, int dtype, int nx, int ny, int ld, hipStream_t 
 // result in dst, the state one step earlier in prev (SGC_ERANGE if larger).
 int diffuse_resident(const void *src, void *dst, void *prev, int dtype, const DiffPlan &p,
                      double alpha, int steps, hipStream_t s);
+// The same for n fields of one shape, one workgroup per field in one launch.
+struct ResidentFields {
+    const void *src[SGC_MAX_NVAR];
+    void *dst[SGC_MAX_NVAR];
+    void *prev[SGC_MAX_NVAR];
+};
+int diffuse_resident_fields(const ResidentFields &f, int n, int dtype, const DiffPlan &p,
+                            double alpha, int steps, hipStream_t s);
 int diffuse_sweep(const void *src, void *dst, int dtype, const DiffPlan &p,
                   double alpha, int map, int steps_in_launch, hipStream_t s);
 // Several fields of the same shape stepped in the same marching launches

@@ -177,8 +177,11 @@ def test_fields_validation(lib):
     assert call(u, v, 2, 7, 8, 8, 8, 0.1, 1, 4, 2, 0) == 3                     # dtype
     assert call(u, v, 2, 1, 8, 8, 7, 0.1, 1, 4, 2, 0) == 1                     # ld < nx
     assert call(u, v, 2, 1, 8, 8, 8, 0.1, 1, 4, 13, 0) == 5                    # time_block
-    for m in (0, 1, 2, 5):                                                     # page maps, resident
+    for m in (0, 1, 2, 6):                                                     # page maps, unknown
         assert call(u, v, 2, 1, 8, 8, 8, 0.1, 1, m, 1, 0) == 1 and "map" in b.last_error()
+    assert call(u, v, 2, 1, 65, 8, 65, 0.1, 1, 5, 1, 0) == 5 and "64 columns" in b.last_error()
+    assert call(u, v, 2, 1, 8, 129, 8, 0.1, 1, 5, 1, 0) == 5 and "128 rows" in b.last_error()
+    assert call(u, v, 2, 1, 8, 8, 8, 0.1, 1 << 31, 5, 1, 0) == 5 and "2^31-1" in b.last_error()
     assert call(_tab(U, 0), v, 2, *base) == 2 and "entry 1" in b.last_error()
     assert call(_tab(U, U + 0x1004), v, 2, *base) == 1 and "aligned" in b.last_error()
     assert call(_tab(U, U + 8 * 63), v, 2, *base) == 4 and "overlap" in b.last_error()  # u[0], u[1]

@@ -74,6 +74,35 @@ def test_fields_equal_single_field_calls(dt):
 
 
 @pytest.mark.parametrize("dt", ["f64", "f32"])
+@pytest.mark.parametrize("nf", [1, 4, 32])
+@pytest.mark.parametrize("nx,ny,ld", [(64, 64, 64), (37, 128, 40), (5, 7, 8), (64, 65, 64)])
+def test_resident_fields(dt, nf, nx, ny, ld):
+    """One workgroup per field: each field as the oracle steps it, and the
+    other buffer one step earlier, as for a single field."""
+    pairs = _fields(nf, nx, ny, ld, dt, 2300 + nx + ny)
+    for steps in (1, 8, 33):
+        say("resident fields", dt, nf, nx, ny, ld, steps)
+        us = [dev(u) for u, _ in pairs]
+        vs = [dev(v) for _, v in pairs]
+        in_v = binding.stencil_diffuse2d_fields(us, vs, nx, 0.1, steps, "resident")
+        torch.cuda.synchronize()
+        for k, (u0, v0) in enumerate(pairs):
+            ref, ref_in_v = oracle_diffuse(u0, v0, nx, 0.1, steps)
+            before, _ = oracle_diffuse(u0, v0, nx, 0.1, steps - 1)
+            assert in_v == ref_in_v
+            assert_bitwise(host(vs[k] if in_v else us[k])[:, :nx], ref[:, :nx], f"resident field {k}")
+            assert_bitwise(host(us[k] if in_v else vs[k])[:, :nx], before[:, :nx], f"resident field {k} prev")
+
+
+def test_resident_fields_reject_large_grids():
+    us = [torch.zeros(129, 8, dtype=torch.float64, device="cuda") for _ in range(2)]
+    vs = [torch.zeros_like(t) for t in us]
+    with pytest.raises(binding.SGCError) as e:
+        binding.stencil_diffuse2d_fields(us, vs, 8, 0.1, 4, "resident")
+    assert e.value.code == 5
+
+
+@pytest.mark.parametrize("dt", ["f64", "f32"])
 def test_max_fields_small_grid(dt):
     pairs = _fields(32, 37, 29, 37, dt, 1700)
     say("32 fields", dt)
