@@ -166,6 +166,43 @@ int check_diffusion_args(const char *fn, int32_t dtype, int64_t nx, int64_t ny, 
     return SGC_OK;
 }
 
+// The march's launch sequence for `steps` sweeps of the fields in `fwd`
+// (u -> v; `back` is v -> u): TILED takes one sweep per launch, TEMPORAL the
+// launch schedule of temporal_launches (the steps spread evenly, an even or
+// odd launch count so that the result lands in v iff steps is odd).  The
+// march treats the edge ring as 0 on read and writes it as 0.
+int march_steps(const FieldPairs &fwd, const FieldPairs &back, int32_t dtype, const DiffPlan &p,
+                double alpha, int64_t steps, int32_t map, int32_t time_block, hipStream_t s) {
+    int rc = SGC_OK;
+    if (map == SGC_DIFF_TILED) {
+        for (int64_t k = 1; k <= steps; ++k)
+            if ((rc = diffuse_sweep_fields((k & 1) ? fwd : back, dtype, p, alpha, map, 1, s))) return rc;
+        return SGC_OK;
+    }
+    const int64_t L = temporal_launches(steps, time_block);
+    const int64_t base = steps / L, extra = steps % L;
+    for (int64_t k = 0; k < L; ++k) {
+        const int ts = (int)(base + (k < extra ? 1 : 0));
+        if ((rc = diffuse_sweep_fields((k & 1) == 0 ? fwd : back, dtype, p, alpha, map, ts, s))) return rc;
+    }
+    return SGC_OK;
+}
+
+// The resident map for the fields (u[k], v[k]): one workgroup per field, all
+// steps in one launch; the result lands in v iff steps is odd and the other
+// buffer ends one step earlier.
+int resident_steps(void *const *u, void *const *v, int32_t n, int32_t dtype, const DiffPlan &p,
+                   double alpha, int64_t steps, hipStream_t s) {
+    const bool odd = (steps & 1) != 0;
+    ResidentFields r{};
+    for (int32_t k = 0; k < n; ++k) {
+        r.src[k] = u[k];
+        r.dst[k] = odd ? v[k] : u[k];
+        r.prev[k] = odd ? u[k] : v[k];
+    }
+    return diffuse_resident_fields(r, n, dtype, p, alpha, (int)steps, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -223,25 +260,15 @@ int stencil_diffuse2d(void *u, void *v, int32_t dtype, int64_t nx, int64_t ny, i
         }
     } else if (map == SGC_DIFF_RESIDENT) {
         if (steps > 0x7fffffffLL) return fail(SGC_ERANGE, "stencil_diffuse2d: resident sweep takes at most 2^31-1 steps");
-        const bool odd = (steps & 1) != 0;
-        rc = diffuse_resident(u, odd ? v : u, odd ? u : v, dtype, p, alpha, (int)steps, s);
-        if (rc) return rc;
-    } else if (map == SGC_DIFF_TILED) {
-        // The march treats the ring as 0 on read and writes it as 0.
-        for (int64_t k = 1; k <= steps; ++k) {
-            const bool odd = (k & 1) != 0;
-            rc = diffuse_sweep(odd ? u : v, odd ? v : u, dtype, p, alpha, map, 1, s);
-            if (rc) return rc;
-        }
-    } else {  // TEMPORAL
-        const int64_t L = temporal_launches(steps, time_block);
-        const int64_t base = steps / L, extra = steps % L;
-        for (int64_t k = 0; k < L; ++k) {
-            const int ts = (int)(base + (k < extra ? 1 : 0));
-            const bool fwd = (k & 1) == 0;
-            rc = diffuse_sweep(fwd ? u : v, fwd ? v : u, dtype, p, alpha, map, ts, s);
-            if (rc) return rc;
-        }
+        if ((rc = resident_steps(&u, &v, 1, dtype, p, alpha, steps, s))) return rc;
+    } else {  // TILED, TEMPORAL
+        FieldPairs fwd{}, back{};
+        fwd.n = back.n = 1;
+        fwd.src[0] = u;
+        fwd.dst[0] = v;
+        back.src[0] = v;
+        back.dst[0] = u;
+        if ((rc = march_steps(fwd, back, dtype, p, alpha, steps, map, time_block, s))) return rc;
     }
     if (result_is_v) *result_is_v = (int32_t)(steps & 1);
     return SGC_OK;
@@ -298,28 +325,9 @@ int stencil_diffuse2d_fields(void *const *u, void *const *v, int32_t nvar, int32
         for (int32_t k = 0; k < nvar; ++k)
             if ((rc = diffuse_zero_ring(u[k], dtype, p.nx, p.ny, p.ld, s))) return rc;
     } else if (map == SGC_DIFF_RESIDENT) {
-        // One workgroup per field, every step in one launch; the other buffer
-        // ends with the state one step earlier, as for a single field.
-        const bool odd = (steps & 1) != 0;
-        ResidentFields r{};
-        for (int32_t k = 0; k < nvar; ++k) {
-            r.src[k] = u[k];
-            r.dst[k] = odd ? v[k] : u[k];
-            r.prev[k] = odd ? u[k] : v[k];
-        }
-        if ((rc = diffuse_resident_fields(r, nvar, dtype, p, alpha, (int)steps, s))) return rc;
-    } else if (map == SGC_DIFF_TILED) {
-        // The march treats the ring as 0 on read and writes it as 0.
-        for (int64_t k = 1; k <= steps; ++k)
-            if ((rc = diffuse_sweep_fields((k & 1) ? fwd : back, dtype, p, alpha, map, 1, s))) return rc;
-    } else {  // TEMPORAL: the single-field launch schedule
-        const int64_t L = temporal_launches(steps, time_block);
-        const int64_t base = steps / L, extra = steps % L;
-        for (int64_t k = 0; k < L; ++k) {
-            const int ts = (int)(base + (k < extra ? 1 : 0));
-            if ((rc = diffuse_sweep_fields((k & 1) == 0 ? fwd : back, dtype, p, alpha, map, ts, s)))
-                return rc;
-        }
+        if ((rc = resident_steps(u, v, nvar, dtype, p, alpha, steps, s))) return rc;
+    } else {  // TILED, TEMPORAL
+        if ((rc = march_steps(fwd, back, dtype, p, alpha, steps, map, time_block, s))) return rc;
     }
     if (result_is_v) *result_is_v = (int32_t)(steps & 1);
     return SGC_OK;

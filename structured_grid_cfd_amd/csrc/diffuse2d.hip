@@ -824,15 +824,6 @@ int diffuse_resident_fields(const ResidentFields &f, int n, int dtype, const Dif
     return resident_t<float>(f, n, p, alpha, steps, s);
 }
 
-int diffuse_resident(const void *src, void *dst, void *prev, int dtype, const DiffPlan &p, double alpha,
-                     int steps, hipStream_t s) {
-    ResidentFields f{};
-    f.src[0] = src;
-    f.dst[0] = dst;
-    f.prev[0] = prev;
-    return diffuse_resident_fields(f, 1, dtype, p, alpha, steps, s);
-}
-
 int diffuse_sweep(const void *src, void *dst, int dtype, const DiffPlan &p, double alpha, int map,
                   int steps_in_launch, hipStream_t s) {
     if (dtype == SGC_F64) return sweep_t<double>(src, dst, p, alpha, map, steps_in_launch, s);

@@ -59,11 +59,9 @@ struct DiffPlan {
     int tile_rows;   // 0 = automatic
 };
 int diffuse_zero_ring(void *buf, int dtype, int nx, int ny, int ld, hipStream_t s);
-// All `steps` steps of a grid of at most 64 x 128 cells in one launch: the
-// result in dst, the state one step earlier in prev (SGC_ERANGE if larger).
-int diffuse_resident(const void *src, void *dst, void *prev, int dtype, const DiffPlan &p,
-                     double alpha, int steps, hipStream_t s);
-// The same for n fields of one shape, one workgroup per field in one launch.
+// All `steps` steps of grids of at most 64 x 128 cells in one launch, one
+// workgroup per field: field k's result in dst[k], the state one step earlier
+// in prev[k] (SGC_ERANGE if larger).
 struct ResidentFields {
     const void *src[SGC_MAX_NVAR];
     void *dst[SGC_MAX_NVAR];
