@@ -3,25 +3,30 @@
 // Operation (Qiita "Fortran 2018でGPUを高速化する Part 3", section 3):
 //   v(i,j) = u(i,j) + alpha*(u(i-1,j) + u(i+1,j) + u(i,j-1) + u(i,j+1) - 4u(i,j))
 // on interior cells, edges fixed at 0, column-major storage with i contiguous
-// (section 4).  Five thread mappings:
+// (section 4).  Thread mappings:
 //   * k_collapse_branch, k_contig, k_strided -- the three loop layouts of
 //     section 5.1-5.3 (flattened grid with an edge branch; workgroup per row
 //     with lanes along i; workgroup per column with lanes along j);
 //   * k_march<T, TS, KV, ...> -- this library's sweep: one wave owns a strip
-//     of 64*K columns (K = 2 elements per lane: one 16-byte FP64 or 8-byte
-//     FP32 load per lane and row) and marches up
-//     a tile of rows, keeping a three-row register window per time level.
-//     West/east neighbours cross lanes with DPP wave shifts, north/south come
-//     from the window, so every input row is read from memory exactly once and
-//     every output row written once per launch.  TS > 1 fuses TS time steps in
-//     one launch (temporal blocking): the strip carries a halo of TS columns on
-//     each side and the tile TS extra rows above and below, recomputed
-//     redundantly, which section 5.4 notes is what a correct fusion across
-//     steps needs.  Every cell of a level is produced by the same expression as
-//     a single step, so all mappings give identical bits.  Memory goes through
-//     raw buffer instructions whose range check supplies the zero rows and
-//     drops stores outside the wave's rows, so the loop has no branches around
-//     memory and its prefetch waits stay partial.
+//     of 64*K columns (K = 2 doubles, or 4 floats at depths 1-2 and 2 floats
+//     from depth 3: one 16- or 8-byte load per lane and row) and marches
+//     along a tile of rows, keeping a three-row register window per time
+//     level.  West/east neighbours cross lanes with DPP wave shifts,
+//     north/south come from the window, so every input row is read from
+//     memory exactly once and every output row written once per launch.
+//     TS > 1 fuses TS time steps in one launch (temporal blocking): the strip
+//     carries a halo of TS columns on each side and the tile TS extra rows
+//     above and below, recomputed redundantly, which section 5.4 notes is
+//     what a correct fusion across steps needs.  Every cell of a level is
+//     produced by the same expression as a single step, so all mappings give
+//     identical bits.  Memory goes through raw buffer instructions whose
+//     range check supplies the zero rows and drops stores outside the wave's
+//     rows, so the loop has no branches around memory and its prefetch waits
+//     stay partial.  A launch may step several fields of one shape: tile t
+//     belongs to field t / field_tiles.
+//   * k_resident<T, R> -- grids of at most 64 x 128 cells held in the
+//     registers of one 1024-thread workgroup for every step of the call, one
+//     workgroup per field.
 #include <atomic>
 #include <climits>
 #include <cmath>
