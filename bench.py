@@ -137,7 +137,7 @@ def main():
         del src, dst
 
     # ---------------- headline: 4096^2, 1000 sweeps per step -----------------
-    c = inputs.cfg2(dtype)
+    c = inputs.uniform_4096(dtype)
     nx, ny, sweeps = c["nx"], c["ny"], c["steps"]
     u = torch.from_numpy(c["u"]).cuda()
     v = torch.from_numpy(c["v"]).cuda()
@@ -314,7 +314,7 @@ def measure_all(log, sections=frozenset({"all"})) -> dict:
         # diffusion, 4096^2: production in both precisions, the page layouts, time blocks
         for dt_name, dt in (("f64", np.float64), ("f32", np.float32)):
             es = 8 if dt_name == "f64" else 4
-            c = inputs.cfg2(dt)
+            c = inputs.uniform_4096(dt)
             nx, ny = c["nx"], c["ny"]
             per_sweep = (nx * ny + (nx - 2) * (ny - 2)) * es
             u0, v0 = dev(c["u"]), dev(c["v"])
@@ -354,7 +354,7 @@ def measure_all(log, sections=frozenset({"all"})) -> dict:
     if want("small"):
         # 64x64 impulse, 32 sweeps: launch/latency bound (production march, and the
         # resident map that runs all sweeps in one workgroup)
-        c = inputs.cfg1()
+        c = inputs.impulse_64()
         u, v = dev(c["u"]), dev(c["v"])
         cfg = launch_config.diffusion("f64", 64, 64)
         t = timed(lambda: binding.stencil_diffuse2d(u, v, 64, 0.1, 32, cfg["map"], cfg["time_block"],
@@ -408,7 +408,7 @@ def measure_all(log, sections=frozenset({"all"})) -> dict:
             log("fields", n, res[f"diffusion_fields_8x{n}_f64_100sweeps"], res[f"diffusion_8_calls_{n}_f64_100sweeps"])
             del us, vs
         # eight 64^2 fields, 32 sweeps, resident map: one workgroup per field
-        c = inputs.cfg1()
+        c = inputs.impulse_64()
         us = [dev(c["u"]) for _ in range(8)]
         vs = [dev(c["v"]) for _ in range(8)]
         work = 8 * 62 * 62 * 32
@@ -432,7 +432,7 @@ def measure_all(log, sections=frozenset({"all"})) -> dict:
 
     if want("large"):
         # 16384^2 FP32, 200 sweeps
-        c = inputs.cfg5_diffusion()
+        c = inputs.uniform_16384_f32()
         u, v = dev(c["u"]), dev(c["v"])
         del c
         cfg = launch_config.diffusion("f32")
@@ -454,7 +454,7 @@ def measure_all(log, sections=frozenset({"all"})) -> dict:
 
     if want("pack"):
         # pack, 8 x 201^3
-        f = dev(inputs.cfg3())
+        f = dev(inputs.fields_201cubed())
         nvar, nz, ny_, nx_ = f.shape
         cv = nvar * nx_ * ny_ * nz
         out = torch.empty(cv, dtype=torch.float64, device="cuda")
@@ -469,7 +469,7 @@ def measure_all(log, sections=frozenset({"all"})) -> dict:
 
     if want("flux"):
         # flux difference, 7 x 201x101x101
-        fi = inputs.cfg4()
+        fi = inputs.faces_201x101x101()
         args = (dev(fi.fx), dev(fi.fy), dev(fi.fz), dev(fi.dx), dev(fi.dy), dev(fi.dz))
         nvar, nxc, nyc, nzc = fi.shape
         cv = nvar * nxc * nyc * nzc
@@ -496,7 +496,7 @@ def measure_all(log, sections=frozenset({"all"})) -> dict:
 
     if want("2d"):
         # 2D workload, 6 x 4800x1200: flux difference and packs along x, y
-        fi = inputs.cfg5_flux()
+        fi = inputs.faces_4800x1200()
         args = (dev(fi.fx), dev(fi.fy), None, dev(fi.dx), dev(fi.dy), None)
         nvar, nxc, nyc, _ = fi.shape
         cv = nvar * nxc * nyc
@@ -516,7 +516,7 @@ def measure_all(log, sections=frozenset({"all"})) -> dict:
         res["flux_stage2d_4800x1200_x6_tiled"] = entry(t, cv, sbytes)
         log("flux2d stage", res["flux_stage2d_4800x1200_x6_tiled"])
         del args, rhs, q0, qs, qo
-        f = dev(inputs.cfg5_fields())
+        f = dev(inputs.fields_4800x1200())
         out = torch.empty(cv, dtype=torch.float64, device="cuda")
         for d, dn in ((0, "x"), (1, "y")):
             for m in ("tiled", "per_cell", "per_cellvar"):

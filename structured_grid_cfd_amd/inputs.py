@@ -13,12 +13,17 @@ Workloads (grid shapes follow the examples named in MFC pull request 2087,
 "Performance" table, and the diffusion setup of Qiita "Fortran 2018でGPUを
 高速化する Part 3", section 3 and Appendix A ``diffusion_common``):
 
-* ``cfg1`` 64x64 FP64, impulse 1 at (33, 33) 1-based, 32 steps.
-* ``cfg2`` 4096x4096 FP64/FP32, interior uniform [0,1), 1000 steps.
-* ``cfg3`` 8 fields of 201^3 FP64, normal(0,1), pack along x/y/z.
-* ``cfg4`` 7 fields on 201x101x101, faces normal(0,1), spacings U[0.5,1.5)/n.
-* ``cfg5`` 6 fields on 4800x1200 (2D flux difference + x/y packs) and
-  16384x16384 FP32 diffusion for 200 steps.
+* ``impulse_64`` 64x64 FP64, impulse 1 at (33, 33) 1-based, 32 steps.
+* ``uniform_4096`` 4096x4096 FP64/FP32, interior uniform [0,1), 1000 steps.
+* ``fields_201cubed`` 8 fields of 201^3 FP64, normal(0,1), pack along x/y/z.
+* ``faces_201x101x101`` 7 fields on 201x101x101, faces normal(0,1), spacings
+  U[0.5,1.5)/n.
+* ``faces_4800x1200`` / ``fields_4800x1200`` 6 fields on 4800x1200 (2D flux
+  difference + x/y packs).
+* ``uniform_16384_f32`` 16384x16384 FP32 diffusion for 200 steps.
+
+Seeds: 1002 (4096^2), 1003 (201^3 fields), 1004 (201x101x101 faces), 1005
+and 1050 (4800x1200 faces and fields), 1006 (16384^2); the impulse draws none.
 
 Array conventions match ``oracle`` and the binding: a 2D grid u(nx, ny) with
 leading dimension ld is a ``(ny, ld)`` array; a field f(j,k,l) is
@@ -122,48 +127,48 @@ def normal_faces(nvar: int, nx: int, ny: int, nz: int, seed: int, two_d: bool = 
 
 
 # ---------------------------------------------------------------------------
-# The five workloads
+# The workloads
 # ---------------------------------------------------------------------------
 
-CFG2_N, CFG2_STEPS = 4096, 1000
-CFG3_NVAR, CFG3_N = 8, 201
-CFG4_NVAR, CFG4_SHAPE = 7, (201, 101, 101)
-CFG5_NVAR, CFG5_SHAPE = 6, (4800, 1200)
-CFG5_DIFF_N, CFG5_DIFF_STEPS = 16384, 200
+UNIFORM_4096_N, UNIFORM_4096_STEPS = 4096, 1000
+FIELDS_201_NVAR, FIELDS_201_N = 8, 201
+FACES_201_NVAR, FACES_201_SHAPE = 7, (201, 101, 101)
+PLANE_4800_NVAR, PLANE_4800_SHAPE = 6, (4800, 1200)
+UNIFORM_16384_N, UNIFORM_16384_STEPS = 16384, 200
 ALPHA = 0.1
 
 
-def cfg1(dtype=np.float64):
+def impulse_64(dtype=np.float64):
     """64x64, impulse at (33,33) 1-based, alpha 0.1, 32 steps."""
     u, v = impulse_grid(64, 64, 33, 33, dtype)
     return dict(u=u, v=v, nx=64, ny=64, alpha=ALPHA, steps=32)
 
 
-def cfg2(dtype=np.float64, steps: int = CFG2_STEPS):
-    u, v = uniform_grid(CFG2_N, CFG2_N, SEED_BASE + 2, dtype)
-    return dict(u=u, v=v, nx=CFG2_N, ny=CFG2_N, alpha=ALPHA, steps=steps)
+def uniform_4096(dtype=np.float64, steps: int = UNIFORM_4096_STEPS):
+    u, v = uniform_grid(UNIFORM_4096_N, UNIFORM_4096_N, SEED_BASE + 2, dtype)
+    return dict(u=u, v=v, nx=UNIFORM_4096_N, ny=UNIFORM_4096_N, alpha=ALPHA, steps=steps)
 
 
-def cfg3():
-    return normal_fields(CFG3_NVAR, CFG3_N, CFG3_N, CFG3_N, SEED_BASE + 3)
+def fields_201cubed():
+    return normal_fields(FIELDS_201_NVAR, FIELDS_201_N, FIELDS_201_N, FIELDS_201_N, SEED_BASE + 3)
 
 
-def cfg4():
-    nx, ny, nz = CFG4_SHAPE
-    return normal_faces(CFG4_NVAR, nx, ny, nz, SEED_BASE + 4)
+def faces_201x101x101():
+    nx, ny, nz = FACES_201_SHAPE
+    return normal_faces(FACES_201_NVAR, nx, ny, nz, SEED_BASE + 4)
 
 
-def cfg5_flux():
-    nx, ny = CFG5_SHAPE
-    return normal_faces(CFG5_NVAR, nx, ny, 1, SEED_BASE + 5, two_d=True)
+def faces_4800x1200():
+    nx, ny = PLANE_4800_SHAPE
+    return normal_faces(PLANE_4800_NVAR, nx, ny, 1, SEED_BASE + 5, two_d=True)
 
 
-def cfg5_fields():
-    nx, ny = CFG5_SHAPE
-    # A second stream on the same config seed family, kept apart from the faces.
-    return normal_fields(CFG5_NVAR, nx, ny, 1, SEED_BASE + 50)
+def fields_4800x1200():
+    nx, ny = PLANE_4800_SHAPE
+    # A second stream of the same workload's seed family, kept apart from the faces.
+    return normal_fields(PLANE_4800_NVAR, nx, ny, 1, SEED_BASE + 50)
 
 
-def cfg5_diffusion(steps: int = CFG5_DIFF_STEPS):
-    u, v = uniform_grid(CFG5_DIFF_N, CFG5_DIFF_N, SEED_BASE + 6, np.float32)
-    return dict(u=u, v=v, nx=CFG5_DIFF_N, ny=CFG5_DIFF_N, alpha=ALPHA, steps=steps)
+def uniform_16384_f32(steps: int = UNIFORM_16384_STEPS):
+    u, v = uniform_grid(UNIFORM_16384_N, UNIFORM_16384_N, SEED_BASE + 6, np.float32)
+    return dict(u=u, v=v, nx=UNIFORM_16384_N, ny=UNIFORM_16384_N, alpha=ALPHA, steps=steps)

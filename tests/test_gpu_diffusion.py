@@ -44,8 +44,8 @@ def _check(u0, v0, nx, alpha, steps, m, tb=1, rows=0, what=""):
 @pytest.mark.parametrize("m,tb", ALL_MAPS)
 @pytest.mark.parametrize("dt", ["f64", "f32"])
 def test_impulse_64x64_32_steps(m, tb, dt):
-    cfg = inputs.cfg1(DT[dt])
-    got = _check(cfg["u"], cfg["v"], 64, cfg["alpha"], cfg["steps"], m, tb, what="cfg1")
+    cfg = inputs.impulse_64(DT[dt])
+    got = _check(cfg["u"], cfg["v"], 64, cfg["alpha"], cfg["steps"], m, tb, what="impulse_64")
     if dt == "f64":
         assert got[32, 32] == 0.025094951021579003  # centre after 32 steps
         assert got.max() == got[32, 32] and got.min() == 0

@@ -60,10 +60,10 @@ def _check_samples(u0, got, nx, alpha, steps, pts):
 
 
 @pytest.mark.parametrize("dt", ["f64", "f32"])
-def test_cfg2_4096_1000_steps_sampled(dt):
-    c = inputs.cfg2(np.float64 if dt == "f64" else np.float32)
+def test_diffusion_4096_1000_steps_sampled(dt):
+    c = inputs.uniform_4096(np.float64 if dt == "f64" else np.float32)
     cfg = launch_config.diffusion(dt)
-    say("cfg2 production", dt, cfg)
+    say("uniform_4096 production", dt, cfg)
     got = _run(c["u"], c["v"], c["nx"], c["alpha"], c["steps"], cfg)
     assert np.all(np.isfinite(got)) and got.min() >= 0 and got.max() < 1
     # an interior window of 2003^2 cells x 1000 steps is the costly one: one
@@ -72,25 +72,25 @@ def test_cfg2_4096_1000_steps_sampled(dt):
 
 
 @pytest.mark.parametrize("dt", ["f64", "f32"])
-def test_cfg2_4096_all_maps_whole_grid_few_steps(dt):
-    c = inputs.cfg2(np.float64 if dt == "f64" else np.float32, steps=6)
+def test_diffusion_4096_all_maps_whole_grid_few_steps(dt):
+    c = inputs.uniform_4096(np.float64 if dt == "f64" else np.float32, steps=6)
     ref = oracle.diffuse2d_result(c["u"], c["nx"], 0.1, 6)
     for m, tb in [("collapse_branch", 1), ("contig", 1), ("strided", 1), ("tiled", 1),
                   ("temporal", 3), ("temporal", 6)]:
-        say("cfg2 6 steps", dt, m, tb)
+        say("uniform_4096 6 steps", dt, m, tb)
         got = _run(c["u"], c["v"], c["nx"], 0.1, 6, {"map": m, "time_block": tb, "tile_rows": 0})
-        assert_bitwise(got, ref, f"cfg2 {m} T={tb}")
+        assert_bitwise(got, ref, f"uniform_4096 {m} T={tb}")
 
 
 @pytest.mark.parametrize("dt", ["f64", "f32"])
-def test_cfg2_all_maps_agree_at_1000_steps(dt):
+def test_diffusion_4096_all_maps_agree_at_1000_steps(dt):
     """The three page layouts and this library's sweeps return one bit
     pattern after the full 1000 steps."""
-    c = inputs.cfg2(np.float64 if dt == "f64" else np.float32)
+    c = inputs.uniform_4096(np.float64 if dt == "f64" else np.float32)
     first = None
     for m, tb in [("temporal", 8), ("tiled", 1), ("contig", 1), ("collapse_branch", 1),
                   ("strided", 1), ("temporal", 12), ("temporal", 5)]:
-        say("cfg2 1000 steps", dt, m, tb)
+        say("uniform_4096 1000 steps", dt, m, tb)
         got = _run(c["u"], c["v"], c["nx"], 0.1, c["steps"], {"map": m, "time_block": tb, "tile_rows": 0})
         if first is None:
             first = got
@@ -98,10 +98,10 @@ def test_cfg2_all_maps_agree_at_1000_steps(dt):
             assert_bitwise(got, first, f"{m} T={tb} vs temporal 8")
 
 
-def test_cfg5_16384_fp32_200_steps_sampled():
-    c = inputs.cfg5_diffusion()
+def test_diffusion_16384_fp32_200_steps_sampled():
+    c = inputs.uniform_16384_f32()
     cfg = launch_config.diffusion("f32")
-    say("cfg5 diffusion production", cfg)
+    say("uniform_16384_f32 production", cfg)
     got = _run(c["u"], c["v"], c["nx"], c["alpha"], c["steps"], cfg)
     assert got.min() >= 0 and got.max() < 1
     _check_samples(c["u"], got, c["nx"], c["alpha"], c["steps"],
@@ -109,53 +109,53 @@ def test_cfg5_16384_fp32_200_steps_sampled():
 
 
 @pytest.mark.parametrize("direction", [0, 1, 2])
-def test_cfg3_pack_201cubed(direction):
-    f = inputs.cfg3()
+def test_pack_8_fields_201cubed(direction):
+    f = inputs.fields_201cubed()
     ref = oracle.field_pack(f, direction)
     fd = dev(f)
     for m in ["tiled", "per_cell", "per_cellvar"]:
-        say("cfg3 pack", direction, m)
+        say("fields_201cubed pack", direction, m)
         out = binding.field_pack(fd, direction, map=m)
         torch.cuda.synchronize()
-        assert_bitwise(host(out), ref, f"cfg3 dir={direction} {m}")
+        assert_bitwise(host(out), ref, f"fields_201cubed dir={direction} {m}")
         del out
 
 
-def test_cfg4_flux_201x101x101():
-    fi = inputs.cfg4()
+def test_flux_7_fields_201x101x101():
+    fi = inputs.faces_201x101x101()
     ref = oracle.flux_diff(fi.fx, fi.fy, fi.fz, fi.dx, fi.dy, fi.dz)
     args = (dev(fi.fx), dev(fi.fy), dev(fi.fz), dev(fi.dx), dev(fi.dy), dev(fi.dz))
     for m in ["tiled", "per_cell", "per_cellvar"]:
-        say("cfg4 flux", m)
+        say("faces_201x101x101 flux", m)
         rhs = binding.flux_diff3d(*args, map=m)
         torch.cuda.synchronize()
-        assert_bitwise(host(rhs), ref, f"cfg4 {m}")
+        assert_bitwise(host(rhs), ref, f"faces_201x101x101 {m}")
 
 
-def test_cfg5_2d_flux_and_packs():
-    fi = inputs.cfg5_flux()
+def test_2d_flux_and_packs_4800x1200():
+    fi = inputs.faces_4800x1200()
     ref = oracle.flux_diff(fi.fx, fi.fy, None, fi.dx, fi.dy, None)
     args = (dev(fi.fx), dev(fi.fy), None, dev(fi.dx), dev(fi.dy), None)
     for m in ["tiled", "per_cell", "per_cellvar"]:
-        say("cfg5 flux", m)
+        say("4800x1200 flux", m)
         rhs = binding.flux_diff3d(*args, map=m)
         torch.cuda.synchronize()
-        assert_bitwise(host(rhs), ref, f"cfg5 flux {m}")
-    f = inputs.cfg5_fields()
+        assert_bitwise(host(rhs), ref, f"4800x1200 flux {m}")
+    f = inputs.fields_4800x1200()
     fd = dev(f)
     for direction in (0, 1):
         pref = oracle.field_pack(f, direction)
         for m in ["tiled", "per_cell", "per_cellvar"]:
-            say("cfg5 pack", direction, m)
+            say("4800x1200 pack", direction, m)
             out = binding.field_pack(fd, direction, map=m)
             torch.cuda.synchronize()
-            assert_bitwise(host(out), pref, f"cfg5 pack dir={direction} {m}")
+            assert_bitwise(host(out), pref, f"4800x1200 pack dir={direction} {m}")
 
 
-def test_cfg4_and_cfg5_flux_stage():
+def test_flux_stage_201x101x101_and_4800x1200():
     """The SSPRK stage fused with the flux difference on the 7 x 201x101x101
     and 6 x 4800x1200 workloads, in the benchmark's launch configuration."""
-    for fi in (inputs.cfg4(), inputs.cfg5_flux()):
+    for fi in (inputs.faces_201x101x101(), inputs.faces_4800x1200()):
         nvar, nx, ny, nz = fi.shape
         g = np.random.Generator(np.random.PCG64(1099))
         q0 = g.standard_normal((nvar, nz, ny, nx))

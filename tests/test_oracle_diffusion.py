@@ -158,7 +158,7 @@ def test_impulse_mass_conserved_until_edges():
     """For the 64x64 impulse workload the total stays 1 while the front has
     not reached the cells next to the edges (the leak after that is far
     below FP64 resolution for 32 steps)."""
-    cfg = inputs.cfg1()
+    cfg = inputs.impulse_64()
     import math
     for steps in (10, 30, 32):
         r = oracle.diffuse2d_result(cfg["u"], 64, 0.1, steps)
