@@ -167,7 +167,13 @@ struct TransArgs {
 
 template <bool UNPACK>
 __global__ __launch_bounds__(256) void k_transpose(TransArgs g) {
-    __shared__ double tile[64][65];
+    // The tile in LDS, sized to this launch's tiles: TY rows of TX values at
+    // an odd stride (in doubles), so that reading a column touches 32
+    // different bank pairs per half-wave.  Smaller tiles leave room for more
+    // workgroups per CU (201 = 4 x 51: 20.8 KB, seven per CU, against four
+    // for a padded 64 x 64 tile).
+    extern __shared__ double tile[];
+    const int ts = g.TX | 1;
     // Variable-major: all XCDs work on one variable's planes at a time, each
     // on a contiguous range of its tiles.
     const int per_var = g.per_var;  // ntx * nty * P rounded up to a multiple of 8
@@ -197,13 +203,14 @@ __global__ __launch_bounds__(256) void k_transpose(TransArgs g) {
         val[i] = buf_load_f64<2>(rin, off);  // each element is read once: non-temporal
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) tile[wv + 4 * i][lane] = val[i];
+    for (int i = 0; i < 16; ++i)
+        if (wv + 4 * i < g.TY && lane < g.TX) tile[(wv + 4 * i) * ts + lane] = val[i];
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const int xx = wv + 4 * i;
         const uint32_t off = (lane < h && xx < w) ? (uint32_t)(lane + xx * g.s_out) * 8u : kOutOfRange;
-        buf_store_f64(tile[lane][xx], rout, off);
+        buf_store_f64(lane < h && xx < w ? tile[lane * ts + xx] : 0.0, rout, off);
     }
 }
 
@@ -266,7 +273,8 @@ int launch_transpose(const PackArgs &a, Layout lay, hipStream_t s) {
     const long tiles = per_var * g.nvar;
     if (tiles > 0x7fffffffL) return fail(SGC_ERANGE, "transpose grid too large");
     g.per_var = (int)per_var;
-    hipLaunchKernelGGL((k_transpose<UNPACK>), dim3((unsigned)tiles), dim3(256), 0, s, g);
+    const size_t lds = (size_t)g.TY * (size_t)(g.TX | 1) * sizeof(double);
+    hipLaunchKernelGGL((k_transpose<UNPACK>), dim3((unsigned)tiles), dim3(256), lds, s, g);
     return check_launch("pack transpose");
 }
 
