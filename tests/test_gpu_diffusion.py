@@ -51,6 +51,36 @@ def test_impulse_64x64_32_steps(m, tb, dt):
         assert got.max() == got[32, 32] and got.min() == 0
 
 
+@pytest.mark.parametrize("m,tb", ALL_MAPS)
+@pytest.mark.parametrize("dt", ["f64", "f32"])
+def test_rounding_ties_and_unfused_products(m, tb, dt):
+    """The two one-step closed forms that fix the rounding order (the oracle
+    pins them by hand), planted at interior and edge-adjacent cells of a
+    zero grid: a tie in ((W + E) + S) + N that only the left-to-right order
+    resolves to 1 - h, and an update c + alpha*t whose product must be
+    rounded before the sum."""
+    dtype = DT[dt]
+    nx, ny = (60, 90) if m == "resident" else (301, 203)
+    h = float(np.finfo(dtype).eps) / 2
+    tie_cells = [(2, 2), (nx // 2, ny // 2), (nx - 2, ny - 3), (min(65, nx // 3), 2), (nx - 2, 2)]
+    u = np.zeros((ny, nx), dtype=dtype)
+    for i, j in tie_cells:
+        u[j, i - 1], u[j - 1, i], u[j + 1, i] = 1.0, h, -h
+    got = _check(u, np.zeros_like(u), nx, 1.0, 1, m, tb, what="sum-order ties")
+    for i, j in tie_cells:
+        assert got[j, i] == dtype(1.0 - h), (i, j)
+
+    p = 30 if dtype == np.float64 else 12
+    t = 1.0 + 2.0 ** -(p + 1)
+    prod_cells = [(2, 1), (nx // 2, ny // 2), (nx - 2, ny - 2), (min(64, nx // 3), 5)]
+    u = np.zeros((ny, nx), dtype=dtype)
+    for i, j in prod_cells:
+        u[j, i], u[j, i - 1] = -1.0, t - 4.0
+    got = _check(u, np.zeros_like(u), nx, 1.0 + 2.0 ** -p, 1, m, tb, what="unfused products")
+    for i, j in prod_cells:
+        assert float(got[j, i]) == 2.0 ** -p + 2.0 ** -(p + 1), (i, j)
+
+
 @pytest.mark.parametrize("steps", [7, 8, 31, 32])
 @pytest.mark.parametrize("m,tb", [(m, 1) for m in PAGE_MAPS + ["tiled", "resident"]] + [("temporal", 4), ("temporal", 12)])
 @pytest.mark.parametrize("dt", ["f64", "f32"])

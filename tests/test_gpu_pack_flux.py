@@ -169,6 +169,33 @@ def test_flux_stage(nvar, nx, ny, nz, two_d):
         assert_bitwise(host(out), ref, f"stage {m}")
 
 
+@pytest.mark.parametrize("two_d", [False, True])
+def test_flux_stage_rounding_order_closed_form(two_d):
+    """The stage's bracket is summed before the scaling by b (the oracle pins
+    this by hand): x faces alternate h, 0 (h half an ulp of 1) across unit
+    cells, every other face is 0, q = 1, q0 = 5, a = 0, b = 3, dt = 1.  Cells
+    with rhs = h give q + h = 1 (a tie to even) and q' = 3 exactly, where
+    b*q + b*dt*rhs would round to 3 + 2^-51."""
+    nvar, nx, ny = 3, 67, 9
+    nz = 1 if two_d else 5
+    h = 2.0 ** -53
+    fx = np.zeros((nvar, nz, ny, nx + 1))
+    fx[..., 0::2] = h
+    fy = np.zeros((nvar, nz, ny + 1, nx))
+    fz = None if two_d else np.zeros((nvar, nz + 1, ny, nx))
+    dx, dy, dz = np.ones(nx), np.ones(ny), None if two_d else np.ones(nz)
+    q0, q = np.full((nvar, nz, ny, nx), 5.0), np.ones((nvar, nz, ny, nx))
+    ref = oracle.flux_stage(fx, fy, fz, dx, dy, dz, q0, q, 0.0, 3.0, 1.0)
+    assert np.all(ref[..., 0::2] == 3.0)
+    args = [dev(fx), dev(fy), dev(fz) if fz is not None else None, dev(dx), dev(dy),
+            dev(dz) if dz is not None else None]
+    for m in MAPS:
+        say("flux stage closed form", two_d, m)
+        out = binding.flux_stage3d(*args, dev(q0), dev(q), 0.0, 3.0, 1.0, map=m)
+        torch.cuda.synchronize()
+        assert_bitwise(host(out), ref, f"stage closed form {m}")
+
+
 @pytest.mark.parametrize("m", MAPS)
 def test_flux_stage_in_place_and_ssprk3(m):
     """q' written over q, then over q0, and a full SSPRK3 step (three stages,

@@ -125,6 +125,41 @@ def test_mirror_symmetry():
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
+def test_sum_order_closed_form(dtype):
+    """One step on values chosen so that the order of the four additions
+    shows in the last bit.  With h half an ulp of 1, W = 1, S = h (row
+    j - 1), N = -h (row j + 1), C = 0 and alpha = 1, the page's expression
+    read left to right gives ((1 + 0) + h) + (-h): 1 + h is a tie and rounds
+    to the even 1, then 1 - h is exact, so v = 1 - h.  Adding N before S, or
+    (W + E) + (S + N), or the vertical pair first all give exactly 1."""
+    h = float(np.finfo(dtype).eps) / 2
+    u = np.zeros((5, 5), dtype=dtype)
+    u[2, 1] = 1.0    # W of cell (i, j) = (2, 2)
+    u[1, 2] = h      # S
+    u[3, 2] = -h     # N
+    r = oracle.diffuse2d_result(u, 5, 1.0, 1)
+    assert r[2, 2] == dtype(1.0 - h)
+
+
+@pytest.mark.parametrize("dtype,p", [(np.float64, 30), (np.float32, 12)])
+def test_update_rounds_product_then_sum(dtype, p):
+    """c + alpha * t rounds the product before the sum (no fused multiply-
+    add).  With alpha = 1 + 2^-p, t = 1 + 2^-(p+1) and c = -1, the exact
+    product is 1 + 2^-p + 2^-(p+1) + 2^-(2p+1); its last term is below half
+    an ulp of 1, so the rounded product drops it and v = 2^-p + 2^-(p+1)
+    exactly, where a fused form would keep 2^-(2p+1).  t comes from
+    W = t - 4 (representable) at the cell (2, 1) of a 4 x 3 grid whose other
+    neighbours are edge cells."""
+    t = 1.0 + 2.0 ** -(p + 1)
+    u = np.zeros((3, 4), dtype=dtype)
+    u[1, 2] = -1.0      # C
+    u[1, 1] = t - 4.0   # W
+    assert float(u[1, 1]) == t - 4.0
+    r = oracle.diffuse2d_result(u, 4, 1.0 + 2.0 ** -p, 1)
+    assert float(r[1, 2]) == 2.0 ** -p + 2.0 ** -(p + 1)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
 def test_maximum_principle_random(dtype):
     """With alpha <= 1/4 each update is a convex combination of
     non-negative values, so 0 <= result <= max(initial) (Appendix A's bound

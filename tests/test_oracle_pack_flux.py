@@ -245,6 +245,25 @@ def test_constant_fluxes_give_the_axpby_exactly():
     assert all(float(e) == float(Fraction(e)) for e in expect.reshape(-1))
 
 
+def test_stage_rounding_order_closed_form():
+    """The stage sums inside the bracket before scaling by b:
+    b*(q + dt*rhs), not b*q + b*dt*rhs.  With rhs = h (half an ulp of 1:
+    faces h and 0 across a unit cell), dt = 1, q = 1, b = 3 and a = 0,
+    q + h is a tie that rounds to the even 1, so q' = 3 exactly; the
+    distributed form gives 3 + 3h, which rounds to 3 + 2^-51.  The z term
+    and the y term are zero; a*q0 = 0."""
+    h = 2.0 ** -53
+    fx = np.array([[[[h, 0.0]]]])        # (nvar, nz, ny, nx + 1)
+    fy = np.zeros((1, 1, 2, 1))
+    fz = np.zeros((1, 2, 1, 1))
+    one = np.ones(1)
+    assert oracle.flux_diff(fx, fy, fz, one, one, one)[0, 0, 0, 0] == h
+    q0 = np.full((1, 1, 1, 1), 5.0)
+    q = np.ones((1, 1, 1, 1))
+    out = oracle.flux_stage(fx, fy, fz, one, one, one, q0, q, 0.0, 3.0, 1.0)
+    assert out[0, 0, 0, 0] == 3.0
+
+
 def test_stage_in_place_equals_out_of_place():
     fi, q0 = _stage_inputs(2, 6, 5, 4, 803)
     q = q0 * 0.5 + 1.0
