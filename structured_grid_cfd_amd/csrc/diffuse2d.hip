@@ -515,9 +515,16 @@ __global__ __launch_bounds__(256) void k_march(MarchArgs g) {
 constexpr int kResidentWaves = 16;
 constexpr int kResidentCols = 64;
 
+// Fast form: when every loaded value is finite and below `fast_limit`, no
+// value, partial sum or product of any step can overflow (the host bounds the
+// growth over all steps), so t - 4c takes one fused multiply-add (exact while
+// 4c is finite) and cells that are never updated take the coefficient 0
+// instead of a select (c = 0 and t finite give c + 0*t = +0).  Otherwise the
+// separate form with per-cell masks runs.  The choice is made once per
+// workgroup, before the first step.
 template <typename T, int R>
 __global__ __launch_bounds__(1024) void k_resident(ResidentFields f, int nx, int ny, int ld, T a,
-                                                   int steps) {
+                                                   int steps, T fast_limit) {
     // One workgroup per field.
     const T *src = static_cast<const T *>(f.src[blockIdx.x]);
     T *dst = static_cast<T *>(f.dst[blockIdx.x]);
@@ -529,39 +536,56 @@ __global__ __launch_bounds__(1024) void k_resident(ResidentFields f, int nx, int
     const bool colin = i >= 1 && i <= nx - 2;
     T val[R];
     bool upd[R];
+    bool small = true;  // every value this lane holds is finite and below fast_limit
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int j = j0 + r;
         upd[r] = colin && j >= 1 && j <= ny - 2;
         val[r] = upd[r] ? src[i + (long)ld * j] : T(0);
+        small = small && __builtin_fabs(val[r]) < fast_limit;  // false for NaN
     }
-    for (int s = 0; s < steps; ++s) {
-        const int set = s & 1;
-        edge[set][w][0][i] = val[0];
-        edge[set][w][1][i] = val[R - 1];
-        __syncthreads();
-        const T below = w > 0 ? edge[set][w - 1][1][i] : T(0);                   // row j0 - 1
-        const T above = w < kResidentWaves - 1 ? edge[set][w + 1][0][i] : T(0);  // row j0 + R
-        if (s == steps - 1) {
+    const bool fast = __syncthreads_and(small) != 0;  // uniform across the workgroup
+    T ae[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) ae[r] = upd[r] ? a : T(0);
+
+    auto run = [&](auto fast_tag) {
+        constexpr bool FAST = decltype(fast_tag)::value;
+        for (int s = 0; s < steps; ++s) {
+            const int set = s & 1;
+            edge[set][w][0][i] = val[0];
+            edge[set][w][1][i] = val[R - 1];
+            __syncthreads();
+            const T below = w > 0 ? edge[set][w - 1][1][i] : T(0);                   // row j0 - 1
+            const T above = w < kResidentWaves - 1 ? edge[set][w + 1][0][i] : T(0);  // row j0 + R
+            if (s == steps - 1) {
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const int j = j0 + r;
+                    if (i < nx && j < ny) prev[i + (long)ld * j] = val[r];
+                }
+            }
+            T nv[R];
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                const int j = j0 + r;
-                if (i < nx && j < ny) prev[i + (long)ld * j] = val[r];
+                const T c = val[r];
+                const T west = wave_shr1(c);
+                const T east = wave_shl1(c);
+                const T south = r == 0 ? below : val[r - 1];
+                const T north = r == R - 1 ? above : val[r + 1];
+                if (FAST)
+                    nv[r] = five_point_fused(west, east, south, north, c, ae[r]);
+                else
+                    nv[r] = upd[r] ? five_point(west, east, south, north, c, a) : T(0);
             }
-        }
-        T nv[R];
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const T c = val[r];
-            const T west = wave_shr1(c);
-            const T east = wave_shl1(c);
-            const T south = r == 0 ? below : val[r - 1];
-            const T north = r == R - 1 ? above : val[r + 1];
-            nv[r] = upd[r] ? five_point(west, east, south, north, c, a) : T(0);
+            for (int r = 0; r < R; ++r) val[r] = nv[r];
         }
-#pragma unroll
-        for (int r = 0; r < R; ++r) val[r] = nv[r];
-    }
+    };
+    if (fast)
+        run(std::true_type{});
+    else
+        run(std::false_type{});
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int j = j0 + r;
@@ -670,6 +694,22 @@ template <typename T> double march_fuse_limit(double alpha, int ts) {
     const double growth = (1.0 + 8.0 * __builtin_fabs(alpha)) * (1.0 + 0x1p-16);
     double lim = sizeof(T) == 8 ? 0x1p1021 : 0x1p125;
     for (int i = 0; i < ts; ++i) lim /= growth;
+    return lim > 0.0 ? lim : 0.0;
+}
+
+// Largest |input| for which the resident kernel's fast form is exact over
+// `steps` steps: every value then stays below 2^(emax-4) (2^1019, 2^123), so
+// 4c, the partial sums and t (at most 8 times the largest value) stay finite
+// and a never-updated cell keeps c + 0*t = +0.  In exact arithmetic a step
+// is v = (1 - 4a) c + a (W + E + S + N), so the largest magnitude grows by at
+// most g = |1 - 4a| + 4|a| (1 for 0 <= a <= 1/4); the six roundings add less
+// than 41 (|a| + 1) units of roundoff u of the old largest magnitude, taken
+// here as 64 (|a| + 1) u.  0 (never fast) when the bound underflows.
+template <typename T> double resident_fast_limit(double alpha, int steps) {
+    const double a = __builtin_fabs(alpha);
+    const double u = sizeof(T) == 8 ? 0x1p-53 : 0x1p-24;
+    const double growth = __builtin_fabs(1.0 - 4.0 * alpha) + 4.0 * a + 64.0 * (a + 1.0) * u;
+    const double lim = (sizeof(T) == 8 ? 0x1p1019 : 0x1p123) * std::pow(growth, -(double)steps);
     return lim > 0.0 ? lim : 0.0;
 }
 
@@ -813,10 +853,11 @@ template <typename T>
 int resident_t(const ResidentFields &f, int n, const DiffPlan &p, double alpha, int steps,
                hipStream_t s) {
     const T a = T(alpha);
+    const T lim = T(resident_fast_limit<T>(alpha, steps));
     if (p.ny <= kResidentWaves * 4)
-        hipLaunchKernelGGL((k_resident<T, 4>), dim3(n), dim3(1024), 0, s, f, p.nx, p.ny, p.ld, a, steps);
+        hipLaunchKernelGGL((k_resident<T, 4>), dim3(n), dim3(1024), 0, s, f, p.nx, p.ny, p.ld, a, steps, lim);
     else
-        hipLaunchKernelGGL((k_resident<T, 8>), dim3(n), dim3(1024), 0, s, f, p.nx, p.ny, p.ld, a, steps);
+        hipLaunchKernelGGL((k_resident<T, 8>), dim3(n), dim3(1024), 0, s, f, p.nx, p.ny, p.ld, a, steps, lim);
     return check_launch("diffusion resident sweep");
 }
 

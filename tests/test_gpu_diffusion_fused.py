@@ -91,3 +91,69 @@ def test_fallback_cells(dt, kind, place):
     for tb, rows in [(8, 16), (5, 0), (12, 24)]:
         ref = _run(u, v, 2 * tb, tb, rows, f"fallback {kind} {place}", nan_ok=True)
         assert not np.isfinite(ref).all()
+
+
+# ---------------------------------------------------------------------------
+# The resident map's fast form (fused t - 4c, zero coefficient on cells it
+# never updates) and its separate form, chosen once per workgroup from the
+# largest input magnitude, the step count and alpha.
+# ---------------------------------------------------------------------------
+
+def _resident(u, v, nx, alpha, steps, what):
+    say("resident", what, u.dtype, u.shape, alpha, steps)
+    got, in_v, uh, vh = gpu_diffuse(u, v, nx, alpha, steps, "resident")
+    ref, ref_in_v = oracle_diffuse(u, v, nx, alpha, steps)
+    assert in_v == ref_in_v
+    assert_bitwise_nan(got[:, :nx], ref[:, :nx], what)
+    before, _ = oracle_diffuse(u, v, nx, alpha, steps - 1)
+    assert_bitwise_nan((uh if in_v else vh)[:, :nx], before[:, :nx], what + " (previous state)")
+    return ref
+
+
+def _signed_small(dt, nx, ny, seed, scale_exp):
+    u, v = inputs.uniform_grid(nx, ny, seed, DT[dt])
+    w = u.copy()
+    w[1:-1, 1:nx - 1] = np.ldexp(u[1:-1, 1:nx - 1] * 2 - 1, scale_exp).astype(DT[dt])
+    return w, v
+
+
+@pytest.mark.parametrize("nx,ny", [(60, 60), (64, 100)])
+@pytest.mark.parametrize("dt,exp,alpha,steps", [
+    ("f64", 1000, 0.1, 33),     # fast: the bound for alpha <= 1/4 barely grows
+    ("f64", 1018, 0.1, 33),     # fast, just below 2^1019
+    ("f64", 1000, 1.0, 10),     # separate: growth 7 per step leaves a limit near 2^991
+    ("f64", 980, 1.0, 10),      # fast again
+    ("f64", -1070, 0.3, 7),     # subnormal, fast
+    ("f32", 120, 0.1, 200),     # fast
+    ("f32", 124, 0.1, 5),       # separate (above 2^123)
+    ("f32", -140, 0.1, 9),      # subnormal, fast
+    ("f32", 100, -0.1, 40),     # negative alpha, growth 1.8: separate
+])
+def test_resident_magnitudes(nx, ny, dt, exp, alpha, steps):
+    u, v = _signed_small(dt, nx, ny, 74 + nx, exp)
+    _resident(u, v, nx, alpha, steps, f"2^{exp} alpha {alpha}")
+
+
+@pytest.mark.parametrize("dt", ["f64", "f32"])
+@pytest.mark.parametrize("kind", ["overflow", "nan", "inf"])
+@pytest.mark.parametrize("place", [(30, 30), (1, 1), (58, 62), (1, 40)])
+def test_resident_separate_form_cells(dt, kind, place):
+    """A cell whose 4c overflows, a NaN or an infinity anywhere in the grid
+    (interior, next to a corner or an edge): the workgroup takes the
+    separate form, and edge cells stay 0 next to NaN and infinite values."""
+    nx, ny = 64, 60
+    u, v = inputs.uniform_grid(nx, ny, 75, DT[dt])
+    j, i = place
+    big = np.ldexp(1.0, 1022 if dt == "f64" else 126)
+    if kind == "overflow":
+        u[j, i] = big
+        for jj, ii in ((j, i - 1), (j, i + 1), (j - 1, i), (j + 1, i)):
+            if 1 <= jj <= ny - 2 and 1 <= ii <= nx - 2:
+                u[jj, ii] = big / 2
+    elif kind == "nan":
+        u[j, i] = np.nan
+    else:
+        u[j, i] = -np.inf
+    ref = _resident(u, v, nx, 0.1, 6, f"separate {kind} {place}")
+    assert not np.isfinite(ref).all()
+    assert (ref[0, :] == 0).all() and (ref[:, 0] == 0).all() and (ref[:, nx - 1] == 0).all()
