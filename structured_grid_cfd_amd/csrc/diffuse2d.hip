@@ -16,13 +16,14 @@
 //     memory exactly once and every output row written once per launch.
 //     TS > 1 fuses TS time steps in one launch (temporal blocking): the strip
 //     carries a halo of TS columns on each side and the tile TS extra rows
-//     above and below, recomputed redundantly, which section 5.4 notes is
-//     what a correct fusion across steps needs.  Every cell of a level is
-//     produced by the same expression as a single step, so all mappings give
-//     identical bits.  Memory goes through raw buffer instructions whose
-//     range check supplies the zero rows and drops stores outside the wave's
-//     rows, so the loop has no branches around memory and its prefetch waits
-//     stay partial.  A launch may step several fields of one shape: tile t
+//     above and below, recomputed redundantly.  (Section 5.4 leaves fusion
+//     across steps out, since one that ignored the neighbour dependencies
+//     would be wrong; the halo carries exactly those dependencies.)  Every
+//     cell of a level is produced by the same expression as a single step,
+//     so all mappings give identical bits.  Memory goes through raw buffer
+//     instructions whose range check supplies the zero rows and drops stores
+//     outside the wave's rows, so the loop has no branches around memory and
+//     its prefetch waits stay partial.  A launch may step several fields of one shape: tile t
 //     belongs to field t / field_tiles.
 //   * k_resident<T, R> -- grids of at most 64 x 128 cells held in the
 //     registers of one 1024-thread workgroup for every step of the call, one
