@@ -127,8 +127,9 @@ typedef enum sgc_dir { SGC_DIR_X = 0, SGC_DIR_Y = 1, SGC_DIR_Z = 2 } sgc_dir;
  * for every map.  The other buffer holds an unspecified earlier state.  Each
  * interior cell is computed as c + alpha*((((W + E) + S) + N) - 4*c) with one
  * rounding per operation, so all maps return the same bits.  (The marching
- * maps form t - 4*c with a fused multiply-add only where that rounds exactly
- * like the separate subtraction, i.e. while 4*c is finite; see diffuse2d.hip.)
+ * and resident maps form t - 4*c with a fused multiply-add only where that
+ * rounds exactly like the separate subtraction, i.e. while 4*c is finite;
+ * see diffuse2d.hip.)
  */
 SGC_API int stencil_diffuse2d(void *u, void *v, int32_t dtype, int64_t nx, int64_t ny,
                       int64_t ld, double alpha, int64_t steps, int32_t map,
