@@ -105,7 +105,7 @@ __global__ __launch_bounds__(256) void k_copy(PackArgs g, int chunks_per_var) {
         constexpr int U8 = 2 * kChunkVec / 256;
         const int e0 = chunk * 2 * kChunkVec;
         double t[U8];
-        if (e0 + 2 * kChunkVec <= n) {  // whole chunk in range
+        if (e0 <= n - 2 * kChunkVec) {  // whole chunk in range (no overflow for n near 2^31)
 #pragma unroll
             for (int u = 0; u < U8; ++u) t[u] = __builtin_nontemporal_load(src + e0 + u * 256 + tid);
 #pragma unroll

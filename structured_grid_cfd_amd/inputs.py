@@ -81,6 +81,41 @@ def uniform_grid(nx: int, ny: int, seed: int, dtype=np.float64, ld: int | None =
     return u, v
 
 
+def _hash_unit(n: int, mult: int, salt: int) -> np.ndarray:
+    """n values k/2^24 in [0, 1) from a multiplicative hash of 0..n-1."""
+    idx = np.arange(n, dtype=np.uint64) + np.uint64(salt)
+    return ((idx * np.uint64(mult)) >> np.uint64(40)).astype(np.float64) / float(1 << 24)
+
+
+def hashed_parts(nx: int, ny: int, dtype=np.float64, salt: int = 0):
+    """Column and row terms (a, b) of ``hashed_grid``: a and b hash the
+    column and row indices with different multipliers, rounded to dtype."""
+    a = _hash_unit(nx, 0x9E3779B97F4A7C15, salt).astype(dtype)
+    b = _hash_unit(ny, 0xC2B2AE3D27D4EB4F, salt).astype(dtype)
+    return a, b
+
+
+def hashed_window(a: np.ndarray, b: np.ndarray, i0: int, i1: int, j0: int, j1: int) -> np.ndarray:
+    """Rows [j0, j1) and columns [i0, i1) of the grid with interior value
+    (a_i + b_j) / 2 (each operation rounded in the dtype of a and b) and
+    edges 0.  The whole grid is the window over every row and column, for
+    sizes of about 2^31 cells that the random generator would take minutes
+    to fill; a device copy of the same grid comes from the same two
+    operations on a and b."""
+    nx, ny = a.size, b.size
+    w = np.add(b[j0:j1, None], a[None, i0:i1])
+    w *= a.dtype.type(0.5)
+    if j0 == 0:
+        w[0, :] = 0
+    if j1 == ny:
+        w[-1, :] = 0
+    if i0 == 0:
+        w[:, 0] = 0
+    if i1 == nx:
+        w[:, -1] = 0
+    return w
+
+
 # ---------------------------------------------------------------------------
 # 3D per-variable fields and face fluxes
 # ---------------------------------------------------------------------------
