@@ -216,7 +216,9 @@ SGC_API int field_unpack(const double *packed, int32_t nvar, int64_t nx, int64_t
  *               Fz (nx,ny,nz+1).  fz == NULL selects the 2D form: nz must be
  *               1, there is no z term and dz must be NULL too.
  *   dx, dy, dz  device cell widths, nx / ny / nz doubles.
- *   nvar        1 .. SGC_MAX_NVAR.   nx, ny, nz >= 1.
+ *   nvar        1 .. SGC_MAX_NVAR.   nx, ny, nz >= 1, with (nx+1)(ny+1)(nz+1)
+ *               (a bound on every face array) and nvar*nx*ny*nz at most
+ *               2^31 - 1 (SGC_ERANGE otherwise).
  *   rhs         device, (nx,ny,nz,nvar) doubles, j fastest; must not overlap
  *               any input.
  *   map         an sgc_var_map.

@@ -11,6 +11,9 @@ float32 operations on a and b (checked against host windows), the result is
 read back only at sampled cells, and each sampled cell is compared bit for bit
 with the oracle run on the sub-grid that holds its whole domain of dependence.
 
+Flux difference: one variable on 1289^3 cells, every face array at
+2.14e9 elements; sampled cells against the oracle's one-cell problem.
+
 Pack: nvar * nx * ny * nz just under 2^31 (2 FP64 fields of 1290 x 1290 x
 645, 8.6 GB each).  The packed arrays are checked on the device against the
 fields' axis permutation (the definition of the y and z orders, a property
@@ -142,4 +145,48 @@ def test_x_pack_copy_at_the_limit_with_mismatched_phase():
     torch.cuda.synchronize()
     assert torch.equal(back.view(torch.int64), f.view(torch.int64))
     del f, buf, out, back
+    torch.cuda.empty_cache()
+
+
+# The flux entry points bound (nx+1)(ny+1)(nz+1), which covers every face
+# array, by 2^31 - 1: 1290^3 = 2^31 - 794648.
+FNX, FNY, FNZ = 1289, 1289, 1289
+assert (FNX + 1) * (FNY + 1) * (FNZ + 1) <= 2 ** 31 - 1
+
+
+def _hashed_device(rows, cols, salt):
+    a, b = inputs.hashed_parts(cols, rows, np.float64, salt=salt)
+    t = (torch.from_numpy(b).cuda()[:, None] + torch.from_numpy(a).cuda()[None, :]).mul_(0.5)
+    return t, a, b
+
+
+@pytest.mark.parametrize("m", ["tiled", "per_cell", "per_cellvar"])
+def test_flux_difference_at_the_element_limit(m):
+    """One variable on 1289^3 cells: face arrays of 2.14e9 elements and
+    (nx+1)(ny+1)(nz+1) at 99.96% of the entry point's 2^31 - 1 bound (17 GB
+    per array).  Sampled cells are compared bit for bit with the
+    oracle run on the one-cell problem made of that cell's six faces and
+    three widths (a cell's value depends on nothing else)."""
+    fx, ax, bx = _hashed_device(FNZ * FNY, FNX + 1, 2035)
+    fy, ay, by = _hashed_device(FNZ * (FNY + 1), FNX, 2036)
+    fz, az, bz = _hashed_device((FNZ + 1) * FNY, FNX, 2037)
+    g = np.random.Generator(np.random.PCG64(2038))
+    dx, dy, dz = (g.uniform(0.5, 1.5, n) / n for n in (FNX, FNY, FNZ))
+    say("max flux", m)
+    rhs = binding.flux_diff3d(fx.view(1, FNZ, FNY, FNX + 1), fy.view(1, FNZ, FNY + 1, FNX),
+                              fz.view(1, FNZ + 1, FNY, FNX), torch.from_numpy(dx).cuda(),
+                              torch.from_numpy(dy).cuda(), torch.from_numpy(dz).cuda(), map=m)
+    torch.cuda.synchronize()
+    face = lambda a, b, row, col: (b[row] + a[col]) * 0.5  # noqa: E731 -- the device's two operations
+    pts = [(0, 0, 0), (FNX - 1, FNY - 1, FNZ - 1), (FNX - 1, 0, FNZ - 1), (0, FNY - 1, FNZ - 1)]
+    pts += [tuple(int(g.integers(0, n)) for n in (FNX, FNY, FNZ)) for _ in range(12)]
+    for j, k, l in pts:
+        cfx = np.array([face(ax, bx, k + FNY * l, j), face(ax, bx, k + FNY * l, j + 1)]).reshape(1, 1, 1, 2)
+        cfy = np.array([face(ay, by, k + (FNY + 1) * l, j),
+                        face(ay, by, k + 1 + (FNY + 1) * l, j)]).reshape(1, 1, 2, 1)
+        cfz = np.array([face(az, bz, k + FNY * l, j), face(az, bz, k + FNY * (l + 1), j)]).reshape(1, 2, 1, 1)
+        ref = oracle.flux_diff(cfx, cfy, cfz, dx[j:j + 1], dy[k:k + 1], dz[l:l + 1])[0, 0, 0, 0]
+        got = rhs[0, l, k, j].item()
+        assert np.float64(got).view(np.uint64) == np.float64(ref).view(np.uint64), (m, j, k, l, got, ref)
+    del fx, fy, fz, rhs
     torch.cuda.empty_cache()
