@@ -25,6 +25,10 @@
  *         per-variable GPU kernels": Changes (the WENO input pack
  *         v_rs_weno(j,k,l,i) = v_vf(i)%sf(j,k,l); the x/y/z flux differences;
  *         inverse grid spacing formed once per cell).
+ *   [Mallard] Mallard documentation, "Design: single-GPU performance and
+ *         parallel scaling": Hardware and method (time steps are SSPRK3, three
+ *         stages) and the Baseline tables (per stage a right-hand side, a
+ *         division by the cell volume and an axpby update).
  *
  * Readings taken where the pages are silent:
  *   - evaluation order of the five-point sum is left to right,
@@ -33,15 +37,16 @@
  *   - the y and z packs are out(k,j,l,var) and out(l,k,j,var), first index
  *     contiguous;
  *   - the flux difference is rhs = (F_lo - F_hi) * (1/d) per direction, summed
- *     in the order x, y, z; cell j's low face is face j, its high face j+1.
- *   [Mallard] Mallard documentation, "Design: single-GPU performance and
- *         parallel scaling": Hardware and method (time steps are SSPRK3, three
- *         stages) and the Baseline tables (per stage a right-hand side, a
- *         division by the cell volume and an axpby update).  The pages give no
- *         stage formula; the reading taken is the Shu-Osher form of SSPRK3,
- *         q' = a*q0 + b*(q + dt*rhs) with (a, b) = (0, 1), (3/4, 1/4),
- *         (1/3, 2/3), evaluated as t = dt*rhs; t = q + t; t = b*t; s = a*q0;
- *         q' = s + t, one rounding each.
+ *     in the order x, y, z; cell j's low face is face j, its high face j+1;
+ *   - the SSPRK stage, for which the pages give no formula, is the Shu-Osher
+ *     form q' = a*q0 + b*(q + dt*rhs) with (a, b) = (0, 1), (3/4, 1/4),
+ *     (1/3, 2/3), evaluated as t = dt*rhs; t = q + t; t = b*t; s = a*q0;
+ *     q' = s + t, one rounding each.
+ *
+ * Every function is pinned by the tests named test_oracle_*: the pages'
+ * printed comparison, hand-worked closed forms, exact rationals on tiny
+ * inputs, permutation and telescoping identities; a mutation test checks
+ * that planted mistakes fail them.
  */
 #include <stddef.h>
 #include <stdlib.h>
