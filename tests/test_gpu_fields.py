@@ -94,6 +94,28 @@ def test_resident_fields(dt, nf, nx, ny, ld):
             assert_bitwise(host(us[k] if in_v else vs[k])[:, :nx], before[:, :nx], f"resident field {k} prev")
 
 
+@pytest.mark.parametrize("dt", ["f64", "f32"])
+def test_resident_fields_choose_their_form_each(dt):
+    """The fast or separate form is chosen per workgroup, that is per field:
+    a NaN in one field and values too large for the fast form in another
+    leave the ordinary fields beside them on the fast form, and every field
+    is the oracle's."""
+    nx, ny = 64, 90
+    pairs = _fields(4, nx, ny, nx, dt, 2400)
+    big = np.ldexp(1.0, 1021 if dt == "f64" else 125)
+    pairs[1][0][40, 30] = np.nan
+    pairs[2][0][20:23, 10:13] = big
+    steps = 9
+    say("resident fields, mixed forms", dt)
+    us = [dev(u) for u, _ in pairs]
+    vs = [dev(v) for _, v in pairs]
+    in_v = binding.stencil_diffuse2d_fields(us, vs, nx, 0.1, steps, "resident")
+    torch.cuda.synchronize()
+    for k, (u0, v0) in enumerate(pairs):
+        ref, _ = oracle_diffuse(u0, v0, nx, 0.1, steps)
+        assert_bitwise_nan(host(vs[k] if in_v else us[k])[:, :nx], ref[:, :nx], f"resident field {k}")
+
+
 def test_resident_fields_reject_large_grids():
     us = [torch.zeros(129, 8, dtype=torch.float64, device="cuda") for _ in range(2)]
     vs = [torch.zeros_like(t) for t in us]
