@@ -11,8 +11,9 @@ float32 operations on a and b (checked against host windows), the result is
 read back only at sampled cells, and each sampled cell is compared bit for bit
 with the oracle run on the sub-grid that holds its whole domain of dependence.
 
-Flux difference: one variable on 1289^3 cells, every face array at
-2.14e9 elements; sampled cells against the oracle's one-cell problem.
+Flux difference and the fused SSPRK stage: one variable on 1289^3 cells,
+every face array at 2.14e9 elements; sampled cells against the oracle's
+one-cell problem.
 
 Pack: nvar * nx * ny * nz just under 2^31 (2 FP64 fields of 1290 x 1290 x
 645, 8.6 GB each).  The packed arrays are checked on the device against the
@@ -189,4 +190,40 @@ def test_flux_difference_at_the_element_limit(m):
         got = rhs[0, l, k, j].item()
         assert np.float64(got).view(np.uint64) == np.float64(ref).view(np.uint64), (m, j, k, l, got, ref)
     del fx, fy, fz, rhs
+    torch.cuda.empty_cache()
+
+
+def test_flux_stage_at_the_element_limit():
+    """The SSPRK stage fused with the flux difference on the same 1289^3
+    problem, q updated in place: sampled cells against the oracle's one-cell
+    stage."""
+    fx, ax, bx = _hashed_device(FNZ * FNY, FNX + 1, 2039)
+    fy, ay, by = _hashed_device(FNZ * (FNY + 1), FNX, 2040)
+    fz, az, bz = _hashed_device((FNZ + 1) * FNY, FNX, 2041)
+    q0, aq0, bq0 = _hashed_device(FNZ * FNY, FNX, 2042)
+    q, aq, bq = _hashed_device(FNZ * FNY, FNX, 2043)
+    g = np.random.Generator(np.random.PCG64(2044))
+    dx, dy, dz = (g.uniform(0.5, 1.5, n) / n for n in (FNX, FNY, FNZ))
+    a, b, dt = 0.75, 0.25, 0.0125
+    say("max flux stage")
+    q4 = q.view(1, FNZ, FNY, FNX)
+    binding.flux_stage3d(fx.view(1, FNZ, FNY, FNX + 1), fy.view(1, FNZ, FNY + 1, FNX),
+                         fz.view(1, FNZ + 1, FNY, FNX), torch.from_numpy(dx).cuda(),
+                         torch.from_numpy(dy).cuda(), torch.from_numpy(dz).cuda(),
+                         q0.view(1, FNZ, FNY, FNX), q4, a, b, dt, out=q4, map="tiled")
+    torch.cuda.synchronize()
+    face = lambda a_, b_, row, col: (b_[row] + a_[col]) * 0.5  # noqa: E731 -- the device's two operations
+    pts = [(0, 0, 0), (FNX - 1, FNY - 1, FNZ - 1), (FNX - 1, 0, FNZ - 1)]
+    pts += [tuple(int(g.integers(0, n)) for n in (FNX, FNY, FNZ)) for _ in range(10)]
+    for j, k, l in pts:
+        cfx = np.array([face(ax, bx, k + FNY * l, j), face(ax, bx, k + FNY * l, j + 1)]).reshape(1, 1, 1, 2)
+        cfy = np.array([face(ay, by, k + (FNY + 1) * l, j),
+                        face(ay, by, k + 1 + (FNY + 1) * l, j)]).reshape(1, 1, 2, 1)
+        cfz = np.array([face(az, bz, k + FNY * l, j), face(az, bz, k + FNY * (l + 1), j)]).reshape(1, 2, 1, 1)
+        cq0 = np.array([face(aq0, bq0, k + FNY * l, j)]).reshape(1, 1, 1, 1)
+        cq = np.array([face(aq, bq, k + FNY * l, j)]).reshape(1, 1, 1, 1)
+        ref = oracle.flux_stage(cfx, cfy, cfz, dx[j:j + 1], dy[k:k + 1], dz[l:l + 1], cq0, cq, a, b, dt)
+        got = q4[0, l, k, j].item()
+        assert np.float64(got).view(np.uint64) == np.float64(ref[0, 0, 0, 0]).view(np.uint64), (j, k, l)
+    del fx, fy, fz, q0, q, q4
     torch.cuda.empty_cache()
