@@ -136,6 +136,11 @@ def test_flux_validation(lib):
     assert lib.flux_diff3d(fx, fy, fz, d, d, d, 1, 4, 4, 4, None, 2, None) == 2
     assert lib.flux_diff3d(fx, fy, fz, d, d, d, 1, 4, 4, 4, U + 0x1000, 2, None) == 4
     assert lib.flux_diff3d(fx, fy, fz, d, d, d, 1, 3000, 3000, 3000, V, 2, None) == 5
+    # the size bound: (nx+1)(ny+1)(nz+1) and nvar*nx*ny*nz at most 2^31 - 1
+    assert lib.flux_diff3d(fx, fy, fz, d, d, d, 1, 1290, 1290, 1290, V, 2, None) == 5  # 1291^3
+    assert lib.flux_diff3d(fx, fy, fz, d, d, d, 1, 1289, 1289, 1289, U, 2, None) == 4  # 1290^3: passes, then the alias
+    fx2, fy2, fz2 = _tab(U, U + 0x800), _tab(U + 0x1000, U + 0x1800), _tab(U + 0x2000, U + 0x2800)
+    assert lib.flux_diff3d(fx2, fy2, fz2, d, d, d, 2, 1289, 1289, 1289, V, 2, None) == 5  # 2 * 1289^3
     assert lib.flux_diff3d(fx, fy, fz, d, d, d, 1, 4, 4, 4, V + 4, 2, None) == 1
     assert lib.flux_diff3d(_tab(U + 2), fy, fz, d, d, d, 1, 4, 4, 4, V, 2, None) == 1
 
