@@ -83,6 +83,8 @@ U, V = 0x10000, 0x90000  # fake, never dereferenced: every call below fails vali
     ((U, V, 1, 8, 8, 8, 0.1, 1, 3, 1, 9), 1, "tile_rows"),
     ((U, V, 1, 8, 8, 8, 0.1, 1, 3, 1, -1), 1, "tile_rows"),
     ((U, V, 1, 70000, 70000, 70000, 0.1, 1, 3, 1, 0), 5, "2^31"),
+    ((U, V, 0, 46341, 46341, 46341, 0.1, 1, 4, 10, 0), 5, "2^31"),       # ld*ny = 2^31 + 4634
+    ((U, U + 8, 0, 46341, 46340, 46341, 0.1, 1, 4, 10, 0), 4, "overlap"),  # 2^31 - 41708: in range
     ((U, V, 1, 65, 8, 65, 0.1, 1, 5, 1, 0), 5, "64 columns"),
     ((U, V, 1, 8, 129, 8, 0.1, 1, 5, 1, 0), 5, "128 rows"),
     ((U, V, 1, 8, 8, 8, 0.1, 1 << 31, 5, 1, 0), 5, "2^31-1 steps"),
@@ -116,6 +118,8 @@ def test_pack_validation(lib):
     assert lib.field_pack(f, 2, 4, 4, 4, 0, V, 3, None) == 1
     assert lib.field_pack(f, 2, 0, 4, 4, 0, V, 2, None) == 1
     assert lib.field_pack(f, 2, 2000, 2000, 1000, 0, V, 2, None) == 5
+    assert lib.field_pack(f, 2, 1290, 1290, 646, 0, V, 2, None) == 5     # 2 * 1290^2 * 646 > 2^31 - 1
+    assert lib.field_pack(f, 2, 1290, 1290, 645, 0, U + 8, 2, None) == 4  # in range, then the alias
     # out overlapping field 1
     assert lib.field_pack(f, 2, 4, 4, 4, 0, U + 0x1000 + 8, 2, None) == 4
     assert lib.field_unpack(V, 2, 4, 4, 4, 1, _tab(U, U + 8), 2, None) == 4
