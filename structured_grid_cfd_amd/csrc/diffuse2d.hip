@@ -501,9 +501,9 @@ __global__ __launch_bounds__(256) void k_march(MarchArgs g) {
 // Resident sweep for small grids: every step in one launch
 // ---------------------------------------------------------------------------
 
-// A grid of at most 64 columns and 16*R rows lives in the registers of one
-// workgroup of sixteen waves: lane i holds column i, wave w holds rows
-// [w*R, w*R + R).  West/east neighbours cross lanes with DPP; north/south
+// A grid of at most 64 columns and W*R rows lives in the registers of one
+// workgroup of W waves (sixteen, or eight for tall FP32 grids): lane i holds
+// column i, wave w holds rows [w*R, w*R + R).  West/east neighbours cross lanes with DPP; north/south
 // come from the lane's own rows, except at a wave's first and last row, whose
 // neighbours are the adjacent waves' last and first rows: each step every
 // wave publishes those two rows in LDS (two slot sets used alternately, so
@@ -523,14 +523,14 @@ constexpr int kResidentCols = 64;
 // instead of a select (c = 0 and t finite give c + 0*t = +0).  Otherwise the
 // separate form with per-cell masks runs.  The choice is made once per
 // workgroup, before the first step.
-template <typename T, int R>
+template <typename T, int R, int W = kResidentWaves>
 __global__ __launch_bounds__(1024) void k_resident(ResidentFields f, int nx, int ny, int ld, T a,
                                                    int steps, T fast_limit) {
     // One workgroup per field.
     const T *src = static_cast<const T *>(f.src[blockIdx.x]);
     T *dst = static_cast<T *>(f.dst[blockIdx.x]);
     T *prev = static_cast<T *>(f.prev[blockIdx.x]);
-    __shared__ T edge[2][kResidentWaves][2][kResidentCols];  // [slot set][wave][first, last row][lane]
+    __shared__ T edge[2][W][2][kResidentCols];  // [slot set][wave][first, last row][lane]
     const int i = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
     const int j0 = w * R;
@@ -558,7 +558,7 @@ __global__ __launch_bounds__(1024) void k_resident(ResidentFields f, int nx, int
             edge[set][w][1][i] = val[R - 1];
             __syncthreads();
             const T below = w > 0 ? edge[set][w - 1][1][i] : T(0);                   // row j0 - 1
-            const T above = w < kResidentWaves - 1 ? edge[set][w + 1][0][i] : T(0);  // row j0 + R
+            const T above = w < W - 1 ? edge[set][w + 1][0][i] : T(0);  // row j0 + R
             if (s == steps - 1) {
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
@@ -855,8 +855,13 @@ int resident_t(const ResidentFields &f, int n, const DiffPlan &p, double alpha, 
                hipStream_t s) {
     const T a = T(alpha);
     const T lim = T(resident_fast_limit<T>(alpha, steps));
+    // Sixteen waves of four or eight rows; FP32 grids taller than 64 rows run
+    // faster as eight waves of sixteen rows (fewer waves at the barrier; the
+    // VALU work per step is smaller than in FP64), FP64 ones slower.
     if (p.ny <= kResidentWaves * 4)
         hipLaunchKernelGGL((k_resident<T, 4>), dim3(n), dim3(1024), 0, s, f, p.nx, p.ny, p.ld, a, steps, lim);
+    else if (sizeof(T) == 4)
+        hipLaunchKernelGGL((k_resident<T, 16, 8>), dim3(n), dim3(512), 0, s, f, p.nx, p.ny, p.ld, a, steps, lim);
     else
         hipLaunchKernelGGL((k_resident<T, 8>), dim3(n), dim3(1024), 0, s, f, p.nx, p.ny, p.ld, a, steps, lim);
     return check_launch("diffusion resident sweep");
