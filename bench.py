@@ -352,18 +352,19 @@ def measure_all(log, sections=frozenset({"all"})) -> dict:
             torch.cuda.empty_cache()
 
     if want("small"):
-        # 64x64 impulse, 32 sweeps: launch/latency bound (production march, and the
-        # resident map that runs all sweeps in one workgroup)
+        # 64x64 impulse, 32 sweeps: launch/latency bound.  Production is the
+        # resident map (all sweeps in one workgroup); the depth-8 march beside it.
         c = inputs.impulse_64()
         u, v = dev(c["u"]), dev(c["v"])
+        t = timed(lambda: binding.stencil_diffuse2d(u, v, 64, 0.1, 32, "temporal", 8, 0, stream), 10, False)
+        res["diffusion_64_f64_32sweeps_march"] = entry(t, 62 * 62 * 32, (64 * 64 + 62 * 62) * 8 *
+                                                       binding.stencil_diffuse2d_launches(32, "temporal", 8),
+                                                       {"map": "temporal", "time_block": 8})
         cfg = launch_config.diffusion("f64", 64, 64)
-        t = timed(lambda: binding.stencil_diffuse2d(u, v, 64, 0.1, 32, cfg["map"], cfg["time_block"],
-                                                    0, stream), 10, False)
-        res["diffusion_64_f64_32sweeps"] = entry(t, 62 * 62 * 32, (64 * 64 + 62 * 62) * 8 *
-                                                 binding.stencil_diffuse2d_launches(32, cfg["map"], cfg["time_block"]))
-        t = timed(lambda: binding.stencil_diffuse2d(u, v, 64, 0.1, 32, "resident", 1, 0, stream), 10, False)
+        t = timed(lambda: binding.stencil_diffuse2d(u, v, 64, 0.1, 32, cfg["map"], cfg["time_block"], 0, stream),
+                  10, False)
         res["diffusion_64_f64_32sweeps_resident"] = entry(t, 62 * 62 * 32, (64 * 64 + 62 * 62) * 8,
-                                                          {"map": "resident", "launches": 1})
+                                                          {"map": cfg["map"], "launches": 1})
 
         # size sweep, FP64 production map, 100 sweeps: where the small-grid
         # latency floor gives way to throughput

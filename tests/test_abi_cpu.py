@@ -205,3 +205,21 @@ def test_last_error_is_per_call(lib):
     # a later failing call replaces the message
     lib.field_pack(None, 1, 1, 1, 1, 0, V, 0, None)
     assert "fields table" in b.last_error()
+
+
+def test_production_launch_settings():
+    """The production settings per grid size: the resident map for grids of
+    at most 64 x 128 cells, the march at depth 8 below 2^24 cells and at
+    depth 10 from there up (what the benchmark and the full-size parity tests
+    run)."""
+    from structured_grid_cfd_amd import launch_config as lc
+    assert lc.diffusion("f64", 64, 64)["map"] == "resident"
+    assert lc.diffusion("f32", 64, 128)["map"] == "resident"
+    assert lc.diffusion("f64", 65, 64) == {"map": "temporal", "time_block": 8, "tile_rows": 0}
+    assert lc.diffusion("f64", 64, 129)["time_block"] == 8
+    assert lc.diffusion("f64", 4095, 4095)["time_block"] == 8
+    assert lc.diffusion("f64", 4096, 4096) == {"map": "temporal", "time_block": 10, "tile_rows": 0}
+    assert lc.diffusion("f32") == {"map": "temporal", "time_block": 10, "tile_rows": 0}
+    for nx, ny in ((64, 64), (300, 200), (4096, 4096)):
+        c = lc.diffusion("f64", nx, ny)
+        assert b.stencil_diffuse2d_launches(32, c["map"], c["time_block"]) >= 1
