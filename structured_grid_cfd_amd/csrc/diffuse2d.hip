@@ -858,12 +858,14 @@ int resident_t(const ResidentFields &f, int n, const DiffPlan &p, double alpha, 
     // Sixteen waves of four or eight rows; FP32 grids taller than 64 rows run
     // faster as eight waves of sixteen rows (fewer waves at the barrier; the
     // VALU work per step is smaller than in FP64), FP64 ones slower.
-    if (p.ny <= kResidentWaves * 4)
+    if (p.ny <= kResidentWaves * 4) {
         hipLaunchKernelGGL((k_resident<T, 4>), dim3(n), dim3(1024), 0, s, f, p.nx, p.ny, p.ld, a, steps, lim);
-    else if (sizeof(T) == 4)
-        hipLaunchKernelGGL((k_resident<T, 16, 8>), dim3(n), dim3(512), 0, s, f, p.nx, p.ny, p.ld, a, steps, lim);
-    else
-        hipLaunchKernelGGL((k_resident<T, 8>), dim3(n), dim3(1024), 0, s, f, p.nx, p.ny, p.ld, a, steps, lim);
+    } else {
+        if constexpr (sizeof(T) == 4)  // (the FP64 form of this shape is never built)
+            hipLaunchKernelGGL((k_resident<T, 16, 8>), dim3(n), dim3(512), 0, s, f, p.nx, p.ny, p.ld, a, steps, lim);
+        else
+            hipLaunchKernelGGL((k_resident<T, 8>), dim3(n), dim3(1024), 0, s, f, p.nx, p.ny, p.ld, a, steps, lim);
+    }
     return check_launch("diffusion resident sweep");
 }
 
