@@ -2,7 +2,7 @@
 index, row offset and launch-grid computation runs at its limit.
 
 Diffusion: ld * ny just under 2^31 elements (FP32, 46341 x 46340, 8.6 GB per
-buffer), every map.
+buffer), every map, and two such fields in one multi-field launch.
 
 The grid is too large to fill from the random generator in a test, so it is
 the hashed grid of ``inputs.hashed_window``: interior (a_i + b_j) / 2 from
@@ -94,6 +94,42 @@ def test_diffusion_at_the_element_limit(grid, m, tb, steps):
         ref = np.float32(_oracle_cell(a, b, i, j, 0.1, steps))
         assert got.view(np.uint32) == ref.view(np.uint32), (m, i, j, got, ref)
     del u, v
+    torch.cuda.empty_cache()
+
+
+def _device_grid(a, b):
+    ad, bd = torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda()
+    u = torch.empty(b.size, a.size, dtype=torch.float32, device="cuda")
+    for j0 in range(0, b.size, 4096):
+        blk = u[j0:j0 + 4096]
+        torch.add(bd[j0:j0 + 4096, None], ad[None, :], out=blk)
+        blk.mul_(0.5)
+    u[0].zero_()
+    u[-1].zero_()
+    u[:, 0].zero_()
+    u[:, -1].zero_()
+    return u
+
+
+def test_two_fields_at_the_element_limit():
+    """Two 46341 x 46340 FP32 fields stepped in the same depth-10 launch of
+    the multi-field march: sampled cells of each against the oracle."""
+    parts = [inputs.hashed_parts(NX, NY, np.float32, salt=2050 + k) for k in range(2)]
+    us = [_device_grid(a, b) for a, b in parts]
+    vs = [torch.empty_like(u) for u in us]
+    say("max size, two fields")
+    in_v = binding.stencil_diffuse2d_fields(us, vs, NX, 0.1, 10, "temporal", 10)
+    torch.cuda.synchronize()
+    assert not in_v
+    g = np.random.Generator(np.random.PCG64(2052))
+    pts = [(1, 1), (NX - 2, NY - 2), (NX // 2, NY - 2)]
+    pts += [(int(g.integers(1, NX - 1)), int(g.integers(1, NY - 1))) for _ in range(6)]
+    for k, (a, b) in enumerate(parts):
+        for i, j in pts:
+            got = np.float32(us[k][j, i].item())
+            ref = np.float32(_oracle_cell(a, b, i, j, 0.1, 10))
+            assert got.view(np.uint32) == ref.view(np.uint32), (k, i, j, got, ref)
+    del us, vs
     torch.cuda.empty_cache()
 
 
