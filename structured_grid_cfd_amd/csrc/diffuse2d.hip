@@ -25,9 +25,9 @@
 //     outside the wave's rows, so the loop has no branches around memory and
 //     its prefetch waits stay partial.  A launch may step several fields of one shape: tile t
 //     belongs to field t / field_tiles.
-//   * k_resident<T, R> -- grids of at most 64 x 128 cells held in the
-//     registers of one 1024-thread workgroup for every step of the call, one
-//     workgroup per field.
+//   * k_resident<T, R, W> -- grids of at most 64 x 128 cells held in the
+//     registers of one workgroup of W waves (R rows each) for every step of
+//     the call, one workgroup per field.
 #include <atomic>
 #include <climits>
 #include <cmath>
