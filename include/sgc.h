@@ -106,15 +106,14 @@ typedef enum sgc_dir { SGC_DIR_X = 0, SGC_DIR_Y = 1, SGC_DIR_Z = 2 } sgc_dir;
  *   map         an sgc_diff_map.
  *   time_block  steps fused per launch for SGC_DIFF_TEMPORAL, 1 ..
  *               SGC_MAX_TIME_BLOCK (SGC_ERANGE above); ignored by other maps.
- *   tile_rows   rows per wave tile for SGC_DIFF_TILED / SGC_DIFF_TEMPORAL;
- *               0 chooses automatically; otherwise 1 .. ny.  Ignored by the
- *               other maps.  The marching maps address each wave's rows
- *               through a window of 2^30 bytes, so tiles are at most
- *               2^30 / (ld * element size) - 2*time_block - 8 rows; where that
- *               is below 1 (rows of ~45 MB or more) they return SGC_ERANGE
- *               before enqueueing anything, and the page maps still apply.
  *   stream      hipStream_t or NULL.
  *   result_is_v optional out (host): 1 if the result is in v, 0 if in u.
+ *
+ * The marching maps (SGC_DIFF_TILED, SGC_DIFF_TEMPORAL) choose their tile
+ * height automatically here (stencil_diffuse2d_ex takes it explicitly).  They
+ * address each wave's rows through a window of 2^30 bytes, so where a single
+ * tile row would not fit (rows of ~45 MB or more) they return SGC_ERANGE
+ * before enqueueing anything, and the page maps still apply.
  *
  * SGC_DIFF_RESIDENT returns SGC_ERANGE for grids wider than 64 or taller
  * than 128 cells, or for more than 2^31 - 1 steps, before enqueueing
@@ -132,9 +131,25 @@ typedef enum sgc_dir { SGC_DIR_X = 0, SGC_DIR_Y = 1, SGC_DIR_Z = 2 } sgc_dir;
  * see diffuse2d.hip.)
  */
 SGC_API int stencil_diffuse2d(void *u, void *v, int32_t dtype, int64_t nx, int64_t ny,
-                      int64_t ld, double alpha, int64_t steps, int32_t map,
-                      int32_t time_block, int32_t tile_rows, void *stream,
-                      int32_t *result_is_v);
+                              int64_t ld, double alpha, int64_t steps, int32_t map,
+                              int32_t time_block, void *stream, int32_t *result_is_v);
+
+/*
+ * stencil_diffuse2d_ex -- stencil_diffuse2d with the marching maps' tile
+ * height given by the caller (the same operation, results and errors; the
+ * tile height changes only how the work is split into waves):
+ *
+ *   tile_rows   rows per wave tile for SGC_DIFF_TILED / SGC_DIFF_TEMPORAL;
+ *               0 chooses automatically (what stencil_diffuse2d does);
+ *               otherwise 1 .. ny (SGC_EINVAL outside 0 .. ny).  Ignored by
+ *               the other maps.  Tiles are at most
+ *               2^30 / (ld * element size) - 2*time_block - 8 rows (larger
+ *               values are clamped to that).
+ */
+SGC_API int stencil_diffuse2d_ex(void *u, void *v, int32_t dtype, int64_t nx, int64_t ny,
+                                 int64_t ld, double alpha, int64_t steps, int32_t map,
+                                 int32_t time_block, int32_t tile_rows, void *stream,
+                                 int32_t *result_is_v);
 
 /*
  * stencil_diffuse2d_fields -- the same sweeps applied to nvar independent

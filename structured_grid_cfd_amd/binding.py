@@ -55,9 +55,12 @@ def load() -> ctypes.CDLL:
             f"{LIB_PATH} is missing: build it first (python -m structured_grid_cfd_amd.build)")
     lib = ctypes.CDLL(str(LIB_PATH))
     vp, i32, i64, dbl = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_double
-    lib.stencil_diffuse2d.argtypes = [vp, vp, i32, i64, i64, i64, dbl, i64, i32, i32, i32, vp,
+    lib.stencil_diffuse2d.argtypes = [vp, vp, i32, i64, i64, i64, dbl, i64, i32, i32, vp,
                                       ctypes.POINTER(i32)]
     lib.stencil_diffuse2d.restype = ctypes.c_int
+    lib.stencil_diffuse2d_ex.argtypes = [vp, vp, i32, i64, i64, i64, dbl, i64, i32, i32, i32, vp,
+                                         ctypes.POINTER(i32)]
+    lib.stencil_diffuse2d_ex.restype = ctypes.c_int
     lib.stencil_diffuse2d_fields.argtypes = [vp, vp, i32, i32, i64, i64, i64, dbl, i64, i32, i32, i32,
                                              vp, vp]
     lib.stencil_diffuse2d_fields.restype = ctypes.c_int
@@ -133,15 +136,40 @@ def _dtype_code(t: torch.Tensor) -> int:
 def stencil_diffuse2d(u: torch.Tensor, v: torch.Tensor, nx: int, alpha: float, steps: int,
                       map: str | int = "temporal", time_block: int = 1, tile_rows: int = 0,
                       stream=None) -> bool:
-    """Run ``steps`` sweeps on the (ny, ld) pair; returns True if the result is in v."""
+    """Run ``steps`` sweeps on the (ny, ld) pair; returns True if the result is in v.
+
+    ``tile_rows`` 0 calls the C entry point ``stencil_diffuse2d`` (automatic
+    tile height); any other value calls ``stencil_diffuse2d_ex`` with it.
+    """
     if u.shape != v.shape or u.dtype != v.dtype or u.dim() != 2:
         raise ValueError("u and v must be 2D tensors of one shape and dtype")
     ny, ld = u.shape
     m = DIFF_MAPS[map] if isinstance(map, str) else int(map)
     res = ctypes.c_int32(-1)
-    rc = load().stencil_diffuse2d(_dev_ptr(u), _dev_ptr(v), _dtype_code(u), nx, ny, ld,
-                                  float(alpha), int(steps), m, int(time_block), int(tile_rows),
-                                  _stream_ptr(stream), ctypes.byref(res))
+    if int(tile_rows) == 0:
+        rc = load().stencil_diffuse2d(_dev_ptr(u), _dev_ptr(v), _dtype_code(u), nx, ny, ld,
+                                      float(alpha), int(steps), m, int(time_block),
+                                      _stream_ptr(stream), ctypes.byref(res))
+    else:
+        rc = load().stencil_diffuse2d_ex(_dev_ptr(u), _dev_ptr(v), _dtype_code(u), nx, ny, ld,
+                                         float(alpha), int(steps), m, int(time_block),
+                                         int(tile_rows), _stream_ptr(stream), ctypes.byref(res))
+    _check(rc)
+    return bool(res.value)
+
+
+def stencil_diffuse2d_ex(u: torch.Tensor, v: torch.Tensor, nx: int, alpha: float, steps: int,
+                         map: str | int = "temporal", time_block: int = 1, tile_rows: int = 0,
+                         stream=None) -> bool:
+    """``stencil_diffuse2d_ex``: the sweeps with an explicit tile height."""
+    if u.shape != v.shape or u.dtype != v.dtype or u.dim() != 2:
+        raise ValueError("u and v must be 2D tensors of one shape and dtype")
+    ny, ld = u.shape
+    m = DIFF_MAPS[map] if isinstance(map, str) else int(map)
+    res = ctypes.c_int32(-1)
+    rc = load().stencil_diffuse2d_ex(_dev_ptr(u), _dev_ptr(v), _dtype_code(u), nx, ny, ld,
+                                     float(alpha), int(steps), m, int(time_block), int(tile_rows),
+                                     _stream_ptr(stream), ctypes.byref(res))
     _check(rc)
     return bool(res.value)
 

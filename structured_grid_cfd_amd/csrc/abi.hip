@@ -229,9 +229,9 @@ int64_t stencil_diffuse2d_launches(int64_t steps, int32_t map, int32_t time_bloc
     }
 }
 
-int stencil_diffuse2d(void *u, void *v, int32_t dtype, int64_t nx, int64_t ny, int64_t ld,
-                      double alpha, int64_t steps, int32_t map, int32_t time_block,
-                      int32_t tile_rows, void *stream, int32_t *result_is_v) {
+int stencil_diffuse2d_ex(void *u, void *v, int32_t dtype, int64_t nx, int64_t ny, int64_t ld,
+                         double alpha, int64_t steps, int32_t map, int32_t time_block,
+                         int32_t tile_rows, void *stream, int32_t *result_is_v) {
     clear();
     if (u == nullptr || v == nullptr) return fail(SGC_ENULL, "stencil_diffuse2d: u and v must be non-NULL");
     int rc = check_diffusion_args("stencil_diffuse2d", dtype, nx, ny, ld, alpha, steps, map, time_block,
@@ -272,6 +272,14 @@ int stencil_diffuse2d(void *u, void *v, int32_t dtype, int64_t nx, int64_t ny, i
     }
     if (result_is_v) *result_is_v = (int32_t)(steps & 1);
     return SGC_OK;
+}
+
+// The automatic tile height of the marching maps.
+int stencil_diffuse2d(void *u, void *v, int32_t dtype, int64_t nx, int64_t ny, int64_t ld,
+                      double alpha, int64_t steps, int32_t map, int32_t time_block, void *stream,
+                      int32_t *result_is_v) {
+    return stencil_diffuse2d_ex(u, v, dtype, nx, ny, ld, alpha, steps, map, time_block, 0, stream,
+                                result_is_v);
 }
 
 int stencil_diffuse2d_fields(void *const *u, void *const *v, int32_t nvar, int32_t dtype, int64_t nx,

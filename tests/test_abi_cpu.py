@@ -9,7 +9,7 @@ import pytest
 
 from structured_grid_cfd_amd import binding as b
 
-EXPECTED = ["stencil_diffuse2d", "stencil_diffuse2d_fields", "stencil_diffuse2d_launches", "field_pack", "field_unpack",
+EXPECTED = ["stencil_diffuse2d", "stencil_diffuse2d_ex", "stencil_diffuse2d_fields", "stencil_diffuse2d_launches", "field_pack", "field_unpack",
             "flux_diff3d", "flux_stage3d", "sgc_last_error", "sgc_abi_version"]
 
 
@@ -94,9 +94,52 @@ U, V = 0x10000, 0x90000  # fake, never dereferenced: every call below fails vali
     ((U, U + 4 * 63, 0, 8, 8, 8, 0.1, 1, 3, 1, 0), 4, "overlap"),
 ])
 def test_diffuse_validation(lib, args, code, msg):
-    rc = lib.stencil_diffuse2d(*args, None, None)
+    """stencil_diffuse2d_ex (explicit tile height), and the same case through
+    stencil_diffuse2d, whose argument list has no tile height: every case
+    whose error does not come from the tile height fails the same way, and
+    neither writes the result flag on an error."""
+    res = ctypes.c_int32(-7)
+    rc = lib.stencil_diffuse2d_ex(*args, None, ctypes.byref(res))
     assert rc == code
     assert msg in b.last_error()
+    assert res.value == -7
+    if msg != "tile_rows":
+        rc = lib.stencil_diffuse2d(*args[:10], None, ctypes.byref(res))
+        assert rc == code
+        assert msg in b.last_error()
+        assert res.value == -7
+
+
+def _declared_params(name):
+    import re
+    text = re.sub(r"/\*.*?\*/", "", b.HEADER.read_text(), flags=re.S)
+    m = re.search(r"SGC_API\s+int\s+" + name + r"\s*\((.*?)\);", text, flags=re.S)
+    return [re.split(r"[\s*]+", p.strip())[-1] for p in m.group(1).split(",")]
+
+
+def test_diffuse_signature_is_the_surveyed_one():
+    """stencil_diffuse2d takes (u, v, dtype, nx, ny, ld, alpha, steps, map,
+    time_block, stream, result_is_v): a caller written to that list passes
+    its stream and result pointer in the right places; the tile height is
+    only in stencil_diffuse2d_ex."""
+    assert _declared_params("stencil_diffuse2d") == [
+        "u", "v", "dtype", "nx", "ny", "ld", "alpha", "steps", "map", "time_block", "stream",
+        "result_is_v"]
+    assert _declared_params("stencil_diffuse2d_ex") == [
+        "u", "v", "dtype", "nx", "ny", "ld", "alpha", "steps", "map", "time_block", "tile_rows",
+        "stream", "result_is_v"]
+    assert len(b.load().stencil_diffuse2d.argtypes) == 12
+    assert len(b.load().stencil_diffuse2d_ex.argtypes) == 13
+
+
+def test_diffuse_surveyed_form_reaches_the_result_pointer(lib):
+    """A NULL stream and a result pointer in the surveyed positions: a
+    validation error (ld < nx) is reported without touching the flag, and a
+    valid zero-size request is impossible without a GPU, so the flag is
+    checked on the error path only."""
+    res = ctypes.c_int32(-3)
+    assert lib.stencil_diffuse2d(U, V, 1, 8, 8, 7, 0.1, 3, 4, 10, None, ctypes.byref(res)) == 1
+    assert "ld" in b.last_error() and res.value == -3
 
 
 def _tab(*ptrs):
@@ -199,7 +242,7 @@ def test_fields_validation(lib):
 
 
 def test_last_error_is_per_call(lib):
-    lib.stencil_diffuse2d(0, 0, 1, 8, 8, 8, 0.1, 1, 3, 1, 0, None, None)
+    lib.stencil_diffuse2d(0, 0, 1, 8, 8, 8, 0.1, 1, 3, 1, None, None)
     assert b.last_error() != ""
     assert b.stencil_diffuse2d_launches(3, "tiled", 1) == 3
     # a later failing call replaces the message
