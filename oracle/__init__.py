@@ -22,6 +22,7 @@ Array conventions (all numpy, C-contiguous):
 from __future__ import annotations
 
 import ctypes
+import dataclasses
 import os
 import subprocess
 import time
@@ -227,29 +228,44 @@ def flux_stage(fx, fy, fz, dx, dy, dz, q0, q, a: float, b: float, dt: float,
 
 
 # ---------------------------------------------------------------------------
-# Comparison metrics (Qiita Part 3, section 8 and 8.1: max abs, RMSE,
-# relative L2, mass difference, worst index, failures under
-# |ref - test| <= atol + rtol*|ref|).
+# How far one field lies from another (Qiita "Fortran 2018でGPUを高速化する
+# Part 3", section 8: the per-cell acceptance band atol + rtol*|reference|;
+# section 8.1: the largest error, the error's L2 norm relative to the
+# reference's, the difference of the totals, and the cells outside the band).
 # ---------------------------------------------------------------------------
 
-def compare(ref: np.ndarray, cand: np.ndarray, atol: float, rtol: float) -> dict:
-    """Error metrics of ``cand`` against ``ref`` over all cells, in float64."""
-    import math
-    r = np.asarray(ref, dtype=np.float64).ravel()
-    c = np.asarray(cand, dtype=np.float64).ravel()
-    assert r.shape == c.shape
-    d = np.abs(r - c)
-    sq_err = math.fsum((d * d).tolist())
-    sq_ref = math.fsum((r * r).tolist())
-    return {
-        "max_abs": float(d.max()),
-        "rmse": math.sqrt(sq_err / r.size),
-        "relative_l2": math.sqrt(sq_err / sq_ref) if sq_ref else math.sqrt(sq_err),
-        "mass_difference": math.fsum(c.tolist()) - math.fsum(r.tolist()),
-        "worst_index_0based": int(np.argmax(d)),
-        "failures": int(np.count_nonzero(d > atol + rtol * np.abs(r))),
-        "cells": int(r.size),
-    }
+@dataclasses.dataclass(frozen=True)
+class Deviation:
+    """A candidate field measured against a reference field, in float64."""
+    largest: float      # max over cells of |candidate - reference|
+    l2_ratio: float     # ||candidate - reference||_2 / ||reference||_2
+    total_shift: float  # sum(candidate) - sum(reference)
+    outside_band: int   # cells with |candidate - reference| > atol + rtol*|reference|
+    n: int              # cells compared
+
+
+def deviation(reference: np.ndarray, candidate: np.ndarray, atol: float, rtol: float) -> Deviation:
+    """Measure ``candidate`` against ``reference`` over every cell.
+
+    Both are widened to float64 first.  The L2 ratio needs a reference that
+    is not identically zero.  The total shift is the sum of the per-cell
+    differences, which equals the difference of the two totals.
+    """
+    ref = np.asarray(reference, dtype=np.float64).reshape(-1)
+    cand = np.asarray(candidate, dtype=np.float64).reshape(-1)
+    if ref.shape != cand.shape:
+        raise ValueError("reference and candidate hold different numbers of cells")
+    diff = cand - ref
+    size = np.abs(diff)
+    ref_norm = float(np.linalg.norm(ref))
+    if ref_norm == 0.0:
+        raise ValueError("the L2 ratio is undefined for an all-zero reference")
+    band = atol + rtol * np.abs(ref)
+    return Deviation(largest=float(size.max(initial=0.0)),
+                     l2_ratio=float(np.linalg.norm(diff)) / ref_norm,
+                     total_shift=float(np.sum(diff)),
+                     outside_band=int((size > band).sum()),
+                     n=int(ref.size))
 
 
 def timed(fn, *args, **kw):

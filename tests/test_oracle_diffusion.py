@@ -32,11 +32,12 @@ def test_printed_fp32_vs_fp64_example():
     u32, _ = inputs.impulse_grid(nx, ny, i1, j1, np.float32)
     r64 = oracle.diffuse2d_result(u64, nx, g["alpha"], steps)
     r32 = oracle.diffuse2d_result(u32, nx, g["alpha"], steps)
-    m = oracle.compare(r64, r32, g["atol"], g["rtol"])
-    for key in ("max_abs", "relative_l2", "mass_difference"):
-        assert f"{m[key]:.6e}" == f"{g[key]:.6e}", (key, m[key], g[key])
-    assert m["cells"] == g["cells"]
-    assert m["failures"] == g["failures"]
+    d = oracle.deviation(r64, r32, g["atol"], g["rtol"])
+    for got, key in ((d.largest, "max_abs"), (d.l2_ratio, "relative_l2"),
+                     (d.total_shift, "mass_difference")):
+        assert f"{got:.6e}" == f"{g[key]:.6e}", (key, got, g[key])
+    assert d.n == g["cells"]
+    assert d.outside_band == g["failures"]
 
 
 def test_printed_example_discriminates_summation_order():
@@ -55,8 +56,8 @@ def test_printed_example_discriminates_summation_order():
             u, v = v, u
         return u
 
-    m = oracle.compare(pairwise(np.float64), pairwise(np.float32), 1e-6, 1e-4)
-    assert f"{m['max_abs']:.6e}" != f"{g['max_abs']:.6e}"
+    d = oracle.deviation(pairwise(np.float64), pairwise(np.float32), 1e-6, 1e-4)
+    assert f"{d.largest:.6e}" != f"{g['max_abs']:.6e}"
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
