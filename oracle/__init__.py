@@ -131,6 +131,24 @@ def diffuse2d_window(u0: np.ndarray, nx: int, alpha: float, steps: int,
     return res[j - j0, i - i0]
 
 
+def diffuse2d_rows(u0: np.ndarray, nx: int, alpha: float, steps: int, j0: int, j1: int) -> np.ndarray:
+    """Rows ``[j0, j1)`` of the full-grid result, computed on a band of rows.
+
+    The same domain-of-dependence argument as :func:`diffuse2d_window`: the
+    band keeps every row within ``steps`` of the requested ones, and a cut
+    edge of the band lies more than ``steps`` rows away from them, so its
+    artificial zero never reaches them.  Columns are not cut.  The returned
+    array is ``(j1 - j0, ld)``.
+    """
+    ny = u0.shape[0]
+    assert 0 <= j0 < j1 <= ny
+    r = steps + 1
+    b0, b1 = max(0, j0 - r), min(ny, j1 + r)
+    band = np.ascontiguousarray(u0[b0:b1])
+    res = diffuse2d_result(band, nx, alpha, steps)
+    return res[j0 - b0:j1 - b0]
+
+
 # ---------------------------------------------------------------------------
 # Directional pack / unpack
 # ---------------------------------------------------------------------------

@@ -265,3 +265,23 @@ def test_zero_steps_is_identity_with_zero_edges():
     u, _ = inputs.uniform_grid(9, 9, seed=1, dtype=np.float32)
     r = oracle.diffuse2d_result(u, 9, 0.1, 0)
     assert np.array_equal(r, u)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_sub_grid_helpers_equal_the_whole_grid(dtype):
+    """The cell window and the row band that the full-size GPU tests use to
+    reach single cells and whole bands of large grids return exactly the
+    whole-grid oracle's bits: a cut edge lies farther than the step count from
+    every kept cell.  Bands that touch the grid's first or last row, bands in
+    the middle, and windows at corners, edges and the interior."""
+    nx, ny, steps = 37, 61, 9
+    u0, _ = inputs.uniform_grid(nx, ny, 4242, dtype, ld=40)
+    whole = oracle.diffuse2d_result(u0, nx, 0.1, steps)
+    as_bits = lambda a: np.ascontiguousarray(a).view(np.uint64 if dtype == np.float64 else np.uint32)  # noqa: E731
+    edges = list(range(0, ny, 7)) + [ny]
+    for j0, j1 in zip(edges[:-1], edges[1:]):
+        got = oracle.diffuse2d_rows(u0, nx, 0.1, steps, j0, j1)
+        assert np.array_equal(as_bits(got[:, :nx]), as_bits(whole[j0:j1, :nx])), (j0, j1)
+    for i, j in [(1, 1), (nx - 2, ny - 2), (1, ny // 2), (nx // 2, 1), (18, 30), (nx - 2, 11)]:
+        got = oracle.diffuse2d_window(u0, nx, 0.1, steps, i, j)
+        assert as_bits(np.asarray(got)) == as_bits(whole[j, i]), (i, j)
