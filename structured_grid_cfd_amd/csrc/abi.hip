@@ -59,6 +59,33 @@ int check_launch(const char *what) {
     return SGC_OK;
 }
 
+int resident_slots(const void *kernel, int block_threads, SlotCache &cache, int *per_cu, int *cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(SGC_EHIP, "hipGetDevice failed");
+    if (dev >= 0 && dev < kMaxDevices) {
+        const int p = cache.per_cu[dev].load(std::memory_order_relaxed);
+        const int c = cache.cus[dev].load(std::memory_order_relaxed);
+        if (p > 0 && c > 0) {
+            *per_cu = p;
+            *cus = c;
+            return SGC_OK;
+        }
+    }
+    int p = 0, c = 0;
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&p, kernel, block_threads, 0);
+    if (e != hipSuccess) return fail(SGC_EHIP, std::string("occupancy query: ") + hipGetErrorString(e));
+    e = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return fail(SGC_EHIP, std::string("CU count query: ") + hipGetErrorString(e));
+    if (p < 1 || c < 1) return fail(SGC_EHIP, "a kernel cannot be resident on this device");
+    if (dev >= 0 && dev < kMaxDevices) {
+        cache.per_cu[dev].store(p, std::memory_order_relaxed);
+        cache.cus[dev].store(c, std::memory_order_relaxed);
+    }
+    *per_cu = p;
+    *cus = c;
+    return SGC_OK;
+}
+
 }  // namespace sgc
 
 using namespace sgc;

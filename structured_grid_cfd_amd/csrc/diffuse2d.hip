@@ -28,7 +28,6 @@
 //   * k_resident<T, R, W> -- grids of at most 64 x 128 cells held in the
 //     registers of one workgroup of W waves (R rows each) for every step of
 //     the call, one workgroup per field.
-#include <atomic>
 #include <climits>
 #include <cmath>
 
@@ -650,41 +649,6 @@ long march_tile_rows(long ny, long nstrips, int ts, int occupancy, long simds, l
     return best_rows > 0 ? best_rows : cap;
 }
 
-// Resident workgroups of `kernel` per CU and the device's CU count, queried
-// once per device and cached.  A 256-thread workgroup puts one wave on each
-// SIMD of a CU, so workgroups per CU is also waves per SIMD.
-constexpr int kMaxDevices = 64;
-struct SlotCache {
-    std::atomic<int> per_cu[kMaxDevices];
-    std::atomic<int> cus[kMaxDevices];
-};
-int resident_slots(const void *kernel, SlotCache &cache, int *per_cu, int *cus) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return fail(SGC_EHIP, "hipGetDevice failed");
-    if (dev >= 0 && dev < kMaxDevices) {
-        const int p = cache.per_cu[dev].load(std::memory_order_relaxed);
-        const int c = cache.cus[dev].load(std::memory_order_relaxed);
-        if (p > 0 && c > 0) {
-            *per_cu = p;
-            *cus = c;
-            return SGC_OK;
-        }
-    }
-    int p = 0, c = 0;
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&p, kernel, 256, 0);
-    if (e != hipSuccess) return fail(SGC_EHIP, std::string("occupancy query: ") + hipGetErrorString(e));
-    e = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return fail(SGC_EHIP, std::string("CU count query: ") + hipGetErrorString(e));
-    if (p < 1 || c < 1) return fail(SGC_EHIP, "the march kernel cannot be resident on this device");
-    if (dev >= 0 && dev < kMaxDevices) {
-        cache.per_cu[dev].store(p, std::memory_order_relaxed);
-        cache.cus[dev].store(c, std::memory_order_relaxed);
-    }
-    *per_cu = p;
-    *cus = c;
-    return SGC_OK;
-}
-
 // Largest sum of |input| over a wave's loads for which no level of a TS-deep
 // fused launch can bring 4c near overflow.  One level grows the largest
 // magnitude by at most 1 + 8|alpha| exactly, times the rounding of its six
@@ -744,9 +708,11 @@ int launch_march_kv(const FieldPairs &f, const DiffPlan &p, double alpha, hipStr
               reinterpret_cast<uintptr_t>(f.dst[k]) % VB == 0;
     auto kernel = vec ? k_march<T, TS, KV, true, kLoadPolicy, kStorePolicy>
                       : k_march<T, TS, KV, false, kLoadPolicy, kStorePolicy>;
+    // A 256-thread workgroup puts one wave on each SIMD of a CU, so resident
+    // workgroups per CU is also resident waves per SIMD.
     static SlotCache cache[2];
     int per_cu = 0, cus = 0;
-    const int rc = resident_slots(reinterpret_cast<const void *>(kernel), cache[vec], &per_cu, &cus);
+    const int rc = resident_slots(reinterpret_cast<const void *>(kernel), 256, cache[vec], &per_cu, &cus);
     if (rc != SGC_OK) return rc;
     long rows = p.tile_rows;
     if (rows <= 0) {

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
 #include <string>
 
@@ -16,6 +17,16 @@ int fail(int code, const std::string &msg);
 
 // Launch-status check after an enqueue: SGC_EHIP with the runtime's message.
 int check_launch(const char *what);
+
+// Resident workgroups of `kernel` per CU (for `block_threads`-thread
+// workgroups) and the device's CU count, queried once per device and cached
+// in `cache` (one cache per kernel).
+constexpr int kMaxDevices = 64;
+struct SlotCache {
+    std::atomic<int> per_cu[kMaxDevices];
+    std::atomic<int> cus[kMaxDevices];
+};
+int resident_slots(const void *kernel, int block_threads, SlotCache &cache, int *per_cu, int *cus);
 
 // Workgroups are dealt to the 8 XCDs of the chip round-robin (block b runs on
 // XCD b % 8).  This maps the hardware block index to a logical index such that
