@@ -22,9 +22,9 @@ Prints ONE JSON line with:
               average launch duration from HIP events around the sweeps of
               every timed step: algorithmic bytes per launch (one read of the
               grid, one write of its interior) against HBM peak, and its
-              arithmetic (the 6 VALU operations of the exact update per
-              interior cell per fused sweep) against the vector-ALU peak of
-              unpacked operations; `bound` names the one nearer its peak;
+              arithmetic (7 operations of the definition per interior cell per
+              fused sweep) against the vector-ALU peak; `bound` is the ALU for
+              fused depths of five and more, HBM below;
   cpu_baseline  the CPU oracle (one thread, pinned) on a bounded sample of
               the same workload, timed on this host;
   kernels     per-kernel figures for every workload (the 64x64 impulse, the
@@ -53,20 +53,17 @@ sys.path.insert(0, str(ROOT))
 
 METRIC = "cell-var updates/s and achieved HBM GB/s (% of MI355X peak), 1 GPU"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
-# Vector-ALU peak.  Each of the 4 SIMDs of a CU executes one 64-lane VALU
-# instruction every 4 cycles, i.e. one operation per lane per cycle, for
-# plain (unpacked) FP32 and for FP64 alike: 256 CUs x 4 SIMDs x 16 lanes x
-# 2.4 GHz = 39.3 T operations/s.  The published 78.6 TFLOP/s FP64 counts an
-# FMA as 2 flops on that rate; the published 157.3 TFLOP/s FP32 also counts
-# the two-wide packed FP32 instructions, which this library never issues (its
-# build disables them).  The stencil's exact update takes 6 such operations
-# per interior cell and sweep: three adds, one FMA forming t - 4c (rounded
-# exactly as the separate product and subtraction), one multiply, one add;
-# the definition counts 7 flops.
-VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
-OPS_PER_UPDATE = 6
-FLOPS_PER_UPDATE = 7  # W+E, +S, +N, 4*C, -, alpha*t, C+
-FLOP_PEAK_TFLOPS = {"f64": 78.6, "f32_unpacked": 78.6}
+# Vector-ALU peaks in operations per second, one operation being one lane of
+# one VALU instruction (an FMA is one operation, two flops).  A SIMD issues a
+# 64-lane VALU instruction per 4 cycles, and gfx950 can issue two FP32 VALU
+# instructions in one 4-cycle slot (the profiler counts such slots as
+# SQ_ACTIVE_INST_VALU2): 256 CUs x 4 SIMDs x 16 lanes x 2 x 2.4 GHz =
+# 78.6 T operations/s for FP32, the published 157.3 TFLOP/s counted with FMAs
+# as two flops; FP64 issues one per slot, 39.3 T operations/s (78.6 TFLOP/s).
+# The five-point update is 7 operations of its definition per interior cell
+# and sweep (W+E, +S, +N, 4*C, -, alpha*t, C+).
+ALU_PEAK_TOPS = {"f64": 256 * 4 * 16 * 2.4e9 / 1e12, "f32": 256 * 4 * 16 * 2 * 2.4e9 / 1e12}
+OPS_PER_UPDATE = 7
 PROFILE_COUNTERS = ROOT / "profiles" / "diffusion_march_counters.json"
 
 # The pages' own figures for related work on other hardware: context for the
@@ -101,7 +98,8 @@ def parse():
                    help="sweeps of the 16384^2 grid in the CPU-baseline sample (of the step's 200)")
     p.add_argument("--kernels", default="all",
                    help="comma-separated sections of the per-kernel table: copy, diffusion "
-                        "(4096^2), small (64^2 and the size sweep), fields (eight fields per call), "
+                        "(4096^2; prod4096 for its production runs only), small (64^2 and the size "
+                        "sweep), fields (eight fields per call), "
                         "large (16384^2 single sweeps), pack, flux, 2d (4800x1200 flux and packs), "
                         "or all")
     p.add_argument("--ref-copy", action="store_true",
@@ -321,17 +319,20 @@ def main():
     sweeps_per_launch = w.sweeps / launches
     hbm_gbs = w.launch_bytes / avg_launch_s / 1e9
     alu_tops = OPS_PER_UPDATE * w.cells * sweeps_per_launch / avg_launch_s / 1e12
-    alu_peak = VALU_PEAK_TOPS
-    tflops = FLOPS_PER_UPDATE * w.cells * sweeps_per_launch / avg_launch_s / 1e12
+    alu_peak = ALU_PEAK_TOPS["f32"]
     hbm_frac, alu_frac = hbm_gbs / HBM_PEAK_GBS, alu_tops / alu_peak
     traffic = counted_traffic(f"f32_16384_T{cfg['time_block']}") if cfg["map"] == "temporal" else None
     kernel_name = "k_march<float, %d, ...>" % (cfg["time_block"] if cfg["map"] == "temporal" else 1)
-    if hbm_frac >= alu_frac:
+    # Fused depths of five and more are bound by vector-ALU issue (the VALU
+    # counters of the marching kernel show the SIMDs issuing in about 90% of
+    # their cycles); one and two sweeps per launch by HBM.
+    fused = cfg["map"] == "temporal" and cfg["time_block"] >= 5
+    if not fused:
         roofline = {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(hbm_frac, 4), "traffic": traffic}
     else:
         roofline = {"bound": "alu", "achieved": round(alu_tops, 2), "peak": round(alu_peak, 2),
-                    "unit": "T VALU operations/s (6 per update)", "frac": round(alu_frac, 4),
+                    "unit": "T operations/s (7 per update)", "frac": round(alu_frac, 4),
                     "traffic": traffic}
     # A kernel that reads the grid and writes it once per sweep can do at most
     # HBM peak / (8 bytes per FP32 cell per sweep) updates/s.
@@ -340,9 +341,7 @@ def main():
     roofline.update({"kernel": kernel_name, "avg_launch_us": round(avg_launch_s * 1e6, 3),
                      "launches_timed": n_launch, "bytes_per_launch": w.launch_bytes,
                      "hbm_gbs": round(hbm_gbs, 1), "hbm_frac": round(hbm_frac, 4),
-                     "valu_tops": round(alu_tops, 2), "valu_frac": round(alu_frac, 4),
-                     "tflops_7_per_update": round(tflops, 2),
-                     "flop_frac_of_unpacked_fp32_fma_peak": round(tflops / FLOP_PEAK_TFLOPS["f32_unpacked"], 4),
+                     "alu_tops": round(alu_tops, 2), "alu_frac": round(alu_frac, 4),
                      "diffusion_cell_updates_per_s": float("%.4e" % diff_rate),
                      "single_sweep_hbm_bound_cu_s": single_sweep_bound,
                      "diffusion_over_single_sweep_bound": round(diff_rate / single_sweep_bound, 3),
@@ -420,15 +419,15 @@ def measure_all(log, sections=frozenset({"all"}), cpu=True) -> dict:
         return out
 
     def entry(times, work, nbytes, extra=None, ops=None):
-        """Median time, rate, minimal-byte bandwidth; with `ops` (VALU
-        operations per unit of work) also the fraction of the VALU peak."""
+        """Median time, rate, minimal-byte bandwidth; with `ops` = (operations
+        per unit of work, dtype) also the fraction of the vector-ALU peak."""
         med = statistics.median(times)
         d = {"ms": round(med * 1e3, 4), "ms_min": round(min(times) * 1e3, 4),
              "reps": len(times), "cellvar_per_s": float("%.4e" % (work / med)),
              "gbs_minimal": round(nbytes / med / 1e9, 1),
              "hbm_frac": round(nbytes / med / 1e9 / HBM_PEAK_GBS, 4)}
         if ops:
-            d["valu_frac"] = round(ops * work / med / 1e12 / VALU_PEAK_TOPS, 4)
+            d["alu_frac"] = round(ops[0] * work / med / 1e12 / ALU_PEAK_TOPS[ops[1]], 4)
         if extra:
             d.update(extra)
         return d
@@ -480,8 +479,9 @@ def measure_all(log, sections=frozenset({"all"}), cpu=True) -> dict:
                 {"time_block": cfg["time_block"]})
             del uu, vv
 
-    if want("diffusion"):
-        # diffusion, 4096^2: production in both precisions, the page layouts, time blocks
+    if want("diffusion") or want("prod4096"):
+        # diffusion, 4096^2: production in both precisions, the page layouts, time
+        # blocks (section prod4096: the production runs only)
         for dt_name, dt in (("f64", np.float64), ("f32", np.float32)):
             es = 8 if dt_name == "f64" else 4
             c = inputs.uniform_4096(dt)
@@ -506,8 +506,12 @@ def measure_all(log, sections=frozenset({"all"}), cpu=True) -> dict:
                 extra["oracle"] = cpu_entry(lambda: oracle.diffuse2d(uc, vc, nx, 0.1, 100), cells * 100, 3,
                                             "100 of the 1000 sweeps of the same grid")
             res[f"diffusion_4096_{dt_name}_1000sweeps_production"] = entry(t, cells * 1000, per_sweep * L, extra,
-                                                                           ops=OPS_PER_UPDATE)
+                                                                           ops=(OPS_PER_UPDATE, dt_name))
             log(dt_name, "production", res[f"diffusion_4096_{dt_name}_1000sweeps_production"])
+            if not want("diffusion"):
+                del u, v, u0, v0
+                torch.cuda.empty_cache()
+                continue
             for m in ("collapse_branch", "contig", "strided", "tiled"):
                 sw = 100
                 run(m, 1, 2)
@@ -521,7 +525,7 @@ def measure_all(log, sections=frozenset({"all"}), cpu=True) -> dict:
                 t = timed(lambda: run("temporal", tb, sw), 3, False)
                 L = binding.stencil_diffuse2d_launches(sw, "temporal", tb)
                 res[f"diffusion_4096_{dt_name}_temporal_T{tb}"] = entry(
-                    t, cells * sw, per_sweep * L, {"sweeps": sw, "launches": L}, ops=OPS_PER_UPDATE)
+                    t, cells * sw, per_sweep * L, {"sweeps": sw, "launches": L}, ops=(OPS_PER_UPDATE, dt_name))
                 log(dt_name, "T", tb, res[f"diffusion_4096_{dt_name}_temporal_T{tb}"])
             del u, v, u0, v0
             torch.cuda.empty_cache()
@@ -592,7 +596,7 @@ def measure_all(log, sections=frozenset({"all"}), cpu=True) -> dict:
         L = binding.stencil_diffuse2d_launches(200, cfg["map"], cfg["time_block"])
         res["diffusion_16384_f32_200sweeps_production"] = entry(
             t, (nx - 2) * (ny - 2) * 200, per_sweep * L, {"launches": L, "time_block": cfg["time_block"]},
-            ops=OPS_PER_UPDATE)
+            ops=(OPS_PER_UPDATE, "f32"))
         log("16384", res["diffusion_16384_f32_200sweeps_production"])
         t = timed(lambda: binding.stencil_diffuse2d(u, v, nx, 0.1, 10, "tiled", 1, 0, stream), 5, False)
         res["diffusion_16384_f32_tiled_single_sweep"] = entry(

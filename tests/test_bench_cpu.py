@@ -24,7 +24,7 @@ def test_counters_file_names_the_hashed_source():
     js = json.loads((ROOT / "profiles" / "diffusion_march_counters.json").read_text())
     assert (ROOT / js["source"]).exists()
     assert len(js["source_sha"]) == 16
-    assert set(js["per_launch_bytes"]) >= {"f64_T10", "f32_T10"}
+    assert set(js["per_launch_bytes"]) >= {"f32_16384_T10"}
 
 
 def test_more_than_one_gpu_is_refused_with_a_message():
