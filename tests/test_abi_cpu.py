@@ -251,9 +251,10 @@ def test_last_error_is_per_call(lib):
 
 
 def test_production_launch_settings():
-    """The production settings per grid size: the resident map for grids of
-    at most 64 x 128 cells, the march at depth 8 below 2^24 cells and at
-    depth 10 from there up (what the benchmark and the full-size parity tests
+    """The production settings per grid size and precision: the resident map
+    for grids of at most 64 x 128 cells; FP64 marches at depth 8 below 2^24
+    cells and 10 from there up; FP32 at 8 below 2^22, 10 up to 2^24, 12 up to
+    2^26 and 10 beyond (what the benchmark and the full-size parity tests
     run)."""
     from structured_grid_cfd_amd import launch_config as lc
     assert lc.diffusion("f64", 64, 64)["map"] == "resident"
@@ -262,7 +263,17 @@ def test_production_launch_settings():
     assert lc.diffusion("f64", 64, 129)["time_block"] == 8
     assert lc.diffusion("f64", 4095, 4095)["time_block"] == 8
     assert lc.diffusion("f64", 4096, 4096) == {"map": "temporal", "time_block": 10, "tile_rows": 0}
+    assert lc.diffusion("f64", 16384, 16384)["time_block"] == 10
     assert lc.diffusion("f32") == {"map": "temporal", "time_block": 10, "tile_rows": 0}
+    # FP32: 8 below 2^22 cells, 10 up to 2^24, 12 up to 2^26, 10 beyond
+    assert lc.diffusion("f32", 2047, 2048)["time_block"] == 8
+    assert lc.diffusion("f32", 2048, 2048)["time_block"] == 10
+    assert lc.diffusion("f32", 4095, 4096)["time_block"] == 10
+    assert lc.diffusion("f32", 4096, 4096) == {"map": "temporal", "time_block": 12, "tile_rows": 0}
+    assert lc.diffusion("f32", 8191, 8192)["time_block"] == 12
+    assert lc.diffusion("f32", 8192, 8192)["time_block"] == 10
+    assert lc.diffusion("f32", 16384, 16384)["time_block"] == 10
+    assert lc.diffusion("f32", 64, 128)["map"] == "resident"
     for nx, ny in ((64, 64), (300, 200), (4096, 4096)):
         c = lc.diffusion("f64", nx, ny)
         assert b.stencil_diffuse2d_launches(32, c["map"], c["time_block"]) >= 1
