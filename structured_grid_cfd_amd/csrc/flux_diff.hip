@@ -14,8 +14,13 @@
 //     inside (the page's "after");
 //   * TILED -- one thread per (j, k) column marching a run of l planes: the
 //     high z face of plane l is kept in a register as the low face of plane
-//     l+1; 1/dx and 1/dy are formed once per column and 1/dz once per plane
-//     per workgroup (in LDS).  Each workgroup handles one variable and the
+//     l+1; 1/dx and 1/dy are formed once per thread, i.e. per column of one
+//     variable over one run of planes (two planes on most grids), and 1/dz
+//     once per plane per workgroup (in LDS).  Forming them once per column
+//     for every variable (one workgroup per column block and run, variables
+//     in turn) or over longer runs measured slower: the kernel is bound by
+//     the loads it keeps in flight, not by the divisions.  Each workgroup
+//     handles one variable and the
 //     workgroups are ordered variable-major, so at any time the chip streams
 //     the five arrays of about one variable: streaming many arrays at once
 //     (all variables per thread) measured 10-13% slower on MI355X.  The 2D
