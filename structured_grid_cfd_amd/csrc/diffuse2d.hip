@@ -316,7 +316,15 @@ __device__ __forceinline__ bool march(const T *__restrict__ src, T *__restrict__
     T checksum = T(0);  // FUSED: sum of |x| over the lane's loads
 
     // Row r of the input: rows outside [lr0, lr1] read as 0 through the
-    // descriptor range (also rows 0 and ny-1, which are edge rows).
+    // descriptor range (also rows 0 and ny-1, which are edge rows).  Columns
+    // left of column 0 (the first strip's left halo) give wrapped offsets
+    // outside the descriptor and read 0 as well (they are masked anyway).
+    // That relies on no lane holding columns on both sides of column 0: the
+    // compiler may merge a lane's adjacent loads into one wider access, and
+    // the range check of such an access does not wrap, so a merged access
+    // starting left of column 0 also reads 0 for the columns from 0 on.
+    // The halo is a whole number of lane widths (asserted in k_march), so a
+    // lane's columns are all left of column 0 or none are.
     auto load_row = [&](T (&x)[K], int r) {
         const uint32_t roff = (uint32_t)(r - lr0) * row_bytes;
         if (VEC) {
@@ -465,6 +473,7 @@ __global__ __launch_bounds__(256) void k_march(MarchArgs g) {
     constexpr int HALO = march_halo<T, KV>(TS);
     constexpr int OW = march_out_width<T, KV>(TS);
     static_assert(OW > 0, "time block too deep for the strip width");
+    static_assert(HALO % K == 0, "a lane must not hold columns on both sides of column 0");
     const int lane = threadIdx.x & 63;
     // The wave index is uniform across the wave; saying so keeps the tile
     // coordinates, and the buffer descriptors built from them, in SGPRs.
