@@ -418,14 +418,30 @@ def measure_all(log, sections=frozenset({"all"}), cpu=True) -> dict:
             out.append(e0.elapsed_time(e1) / 1e3)
         return out
 
+    def timed_group(fns, reps, do_flush):
+        """Time several variants of one workload, rotating their order on
+        every repetition so that no variant always runs first or last."""
+        names = list(fns)
+        out = {k: [] for k in names}
+        for r in range(reps):
+            for i in range(len(names)):
+                k = names[(i + r) % len(names)]
+                out[k].extend(timed(fns[k], 1, do_flush))
+        return out
+
+    copy_gbs = []  # the reference copy's bandwidth, once measured
+
     def entry(times, work, nbytes, extra=None, ops=None):
-        """Median time, rate, minimal-byte bandwidth; with `ops` = (operations
-        per unit of work, dtype) also the fraction of the vector-ALU peak."""
+        """Median time, rate, minimal-byte bandwidth (also as a fraction of
+        the measured reference copy's); with `ops` = (operations per unit of
+        work, dtype) also the fraction of the vector-ALU peak."""
         med = statistics.median(times)
         d = {"ms": round(med * 1e3, 4), "ms_min": round(min(times) * 1e3, 4),
              "reps": len(times), "cellvar_per_s": float("%.4e" % (work / med)),
              "gbs_minimal": round(nbytes / med / 1e9, 1),
              "hbm_frac": round(nbytes / med / 1e9 / HBM_PEAK_GBS, 4)}
+        if copy_gbs:
+            d["of_copy"] = round(nbytes / med / 1e9 / copy_gbs[0], 4)
         if ops:
             d["alu_frac"] = round(ops[0] * work / med / 1e12 / ALU_PEAK_TOPS[ops[1]], 4)
         if extra:
@@ -436,15 +452,18 @@ def measure_all(log, sections=frozenset({"all"}), cpu=True) -> dict:
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
 
     if want("copy"):
-        # reference: a 16-byte-vector copy of 1 GiB (the x pack of one variable)
-        n = 128 * 1024 * 1024
+        # reference: a 16-byte-vector copy of 2 GiB (the x pack of one
+        # variable); every later entry also reports its bandwidth against it
+        n = 256 * 1024 * 1024
         src = torch.empty((1, 1, 1, n), dtype=torch.float64, device="cuda").fill_(1.0)
         dst = torch.empty_like(src)
         binding.field_pack(src, 0, out=dst)
         t = timed(lambda: binding.field_pack(src, 0, out=dst), 10, True)
-        res["copy_1GiB_dwordx4"] = entry(t, n, 2 * n * 8)
-        log("copy", res["copy_1GiB_dwordx4"])
+        res["copy_2GiB_dwordx4"] = entry(t, n, 2 * n * 8)
+        copy_gbs.append(res["copy_2GiB_dwordx4"]["gbs_minimal"])
+        log("copy", res["copy_2GiB_dwordx4"])
         del src, dst
+        torch.cuda.empty_cache()
 
     if want("small"):
         # 64x64 impulse, 32 sweeps: launch/latency bound.  Production is the
@@ -512,20 +531,24 @@ def measure_all(log, sections=frozenset({"all"}), cpu=True) -> dict:
                 del u, v, u0, v0
                 torch.cuda.empty_cache()
                 continue
-            for m in ("collapse_branch", "contig", "strided", "tiled"):
-                sw = 100
+            maps = ("collapse_branch", "contig", "strided", "tiled")
+            sw = 100
+            for m in maps:
                 run(m, 1, 2)
-                t = timed(lambda: run(m, 1, sw), 3, False)
-                res[f"diffusion_4096_{dt_name}_{m}"] = entry(t, cells * sw, per_sweep * sw,
+            tg = timed_group({m: (lambda m=m: run(m, 1, sw)) for m in maps}, 3, False)
+            for m in maps:
+                res[f"diffusion_4096_{dt_name}_{m}"] = entry(tg[m], cells * sw, per_sweep * sw,
                                                              {"sweeps": sw})
                 log(dt_name, m, res[f"diffusion_4096_{dt_name}_{m}"])
-            for tb in (2, 3, 4, 6, 8, 10, 12):
-                sw = 240
+            depths = (2, 3, 4, 6, 8, 10, 12)
+            sw = 240
+            for tb in depths:
                 run("temporal", tb, sw)
-                t = timed(lambda: run("temporal", tb, sw), 3, False)
+            tg = timed_group({tb: (lambda tb=tb: run("temporal", tb, sw)) for tb in depths}, 3, False)
+            for tb in depths:
                 L = binding.stencil_diffuse2d_launches(sw, "temporal", tb)
                 res[f"diffusion_4096_{dt_name}_temporal_T{tb}"] = entry(
-                    t, cells * sw, per_sweep * L, {"sweeps": sw, "launches": L}, ops=(OPS_PER_UPDATE, dt_name))
+                    tg[tb], cells * sw, per_sweep * L, {"sweeps": sw, "launches": L}, ops=(OPS_PER_UPDATE, dt_name))
                 log(dt_name, "T", tb, res[f"diffusion_4096_{dt_name}_temporal_T{tb}"])
             del u, v, u0, v0
             torch.cuda.empty_cache()
@@ -552,10 +575,11 @@ def measure_all(log, sections=frozenset({"all"}), cpu=True) -> dict:
                                               0, stream)
 
             multi(); separate()
+            tg = timed_group({"multi": multi, "separate": separate}, 5, False)
             res[f"diffusion_fields_8x{n}_f64_100sweeps"] = entry(
-                timed(multi, 5, False), work, nbytes, {"time_block": cfg["time_block"], "launches": L})
+                tg["multi"], work, nbytes, {"time_block": cfg["time_block"], "launches": L})
             res[f"diffusion_8_calls_{n}_f64_100sweeps"] = entry(
-                timed(separate, 5, False), work, nbytes, {"time_block": cfg["time_block"], "launches": 8 * L})
+                tg["separate"], work, nbytes, {"time_block": cfg["time_block"], "launches": 8 * L})
             log("fields", n, res[f"diffusion_fields_8x{n}_f64_100sweeps"], res[f"diffusion_8_calls_{n}_f64_100sweeps"])
             del us, vs
         # eight 64^2 fields, 32 sweeps, resident map: one workgroup per field
@@ -573,9 +597,10 @@ def measure_all(log, sections=frozenset({"all"}), cpu=True) -> dict:
                 binding.stencil_diffuse2d(us[k], vs[k], 64, 0.1, 32, "resident", 1, 0, stream)
 
         rmulti(); rseparate()
-        res["diffusion_fields_8x64_f64_32sweeps_resident"] = entry(timed(rmulti, 10, False), work, nbytes,
+        tg = timed_group({"multi": rmulti, "separate": rseparate}, 10, False)
+        res["diffusion_fields_8x64_f64_32sweeps_resident"] = entry(tg["multi"], work, nbytes,
                                                                    {"map": "resident", "launches": 1})
-        res["diffusion_8_calls_64_f64_32sweeps_resident"] = entry(timed(rseparate, 10, False), work, nbytes,
+        res["diffusion_8_calls_64_f64_32sweeps_resident"] = entry(tg["separate"], work, nbytes,
                                                                   {"map": "resident", "launches": 8})
         log("fields resident", res["diffusion_fields_8x64_f64_32sweeps_resident"],
             res["diffusion_8_calls_64_f64_32sweeps_resident"])
@@ -613,13 +638,15 @@ def measure_all(log, sections=frozenset({"all"}), cpu=True) -> dict:
         cv = nvar * nx_ * ny_ * nz
         out = torch.empty(cv, dtype=torch.float64, device="cuda")
         for d, dn in enumerate("xyz"):
-            for m in ("tiled", "per_cell", "per_cellvar"):
+            maps = ("tiled", "per_cell", "per_cellvar")
+            for m in maps:
                 binding.field_pack(f, d, out=out, map=m)
-                t = timed(lambda: binding.field_pack(f, d, out=out, map=m), 10, True)
+            tg = timed_group({m: (lambda m=m: binding.field_pack(f, d, out=out, map=m)) for m in maps}, 10, True)
+            for m in maps:
                 extra = None
                 if cpu and m == "tiled":
                     extra = {"oracle": cpu_entry(lambda: oracle.field_pack(fh, d), cv, 3, "the whole workload")}
-                res[f"pack_201cubed_x8_{dn}_{m}"] = entry(t, cv, 16 * cv, extra)
+                res[f"pack_201cubed_x8_{dn}_{m}"] = entry(tg[m], cv, 16 * cv, extra)
                 log("pack", dn, m, res[f"pack_201cubed_x8_{dn}_{m}"])
         del f, out, fh
         torch.cuda.empty_cache()
@@ -632,25 +659,29 @@ def measure_all(log, sections=frozenset({"all"}), cpu=True) -> dict:
         cv = nvar * nxc * nyc * nzc
         nbytes = 8 * (fi.fx.size + fi.fy.size + fi.fz.size + cv + nxc + nyc + nzc)
         rhs = torch.empty(cv, dtype=torch.float64, device="cuda").view(nvar, nzc, nyc, nxc)
-        for m in ("tiled", "per_cell", "per_cellvar"):
+        maps = ("tiled", "per_cell", "per_cellvar")
+        for m in maps:
             binding.flux_diff3d(*args, rhs=rhs, map=m)
-            t = timed(lambda: binding.flux_diff3d(*args, rhs=rhs, map=m), 10, True)
+        tg = timed_group({m: (lambda m=m: binding.flux_diff3d(*args, rhs=rhs, map=m)) for m in maps}, 10, True)
+        for m in maps:
             extra = None
             if cpu and m == "tiled":
                 extra = {"oracle": cpu_entry(lambda: oracle.flux_diff(fi.fx, fi.fy, fi.fz, fi.dx, fi.dy, fi.dz),
                                              cv, 3, "the whole workload")}
-            res[f"flux_201x101x101_x7_{m}"] = entry(t, cv, nbytes, extra)
+            res[f"flux_201x101x101_x7_{m}"] = entry(tg[m], cv, nbytes, extra)
             log("flux", m, res[f"flux_201x101x101_x7_{m}"])
         # one SSPRK stage fused with it: reads q0 and q, writes q' instead of rhs
         q0 = dev(inputs.normal_fields(nvar, nxc, nyc, nzc, 1060))
         qs = dev(inputs.normal_fields(nvar, nxc, nyc, nzc, 1061))
         qo = torch.empty_like(qs)
         sbytes = nbytes + 2 * 8 * cv
-        for m in ("tiled", "per_cell", "per_cellvar"):
+        for m in maps:
             binding.flux_stage3d(*args, q0, qs, 0.75, 0.25, 1e-3, out=qo, map=m)
-            t = timed(lambda: binding.flux_stage3d(*args, q0, qs, 0.75, 0.25, 1e-3, out=qo, map=m), 10, True)
+        tg = timed_group({m: (lambda m=m: binding.flux_stage3d(*args, q0, qs, 0.75, 0.25, 1e-3, out=qo, map=m))
+                          for m in maps}, 10, True)
+        for m in maps:
             res[f"flux_stage_201x101x101_x7_{m}"] = entry(
-                t, cv, sbytes, {"note": "a separate update pass would add one write and one read of rhs"})
+                tg[m], cv, sbytes, {"note": "a separate update pass would add one write and one read of rhs"})
             log("flux stage", m, res[f"flux_stage_201x101x101_x7_{m}"])
         del args, rhs, q0, qs, qo
         torch.cuda.empty_cache()
@@ -663,14 +694,16 @@ def measure_all(log, sections=frozenset({"all"}), cpu=True) -> dict:
         cv = nvar * nxc * nyc
         nbytes = 8 * (fi.fx.size + fi.fy.size + cv + nxc + nyc)
         rhs = torch.empty(cv, dtype=torch.float64, device="cuda").view(nvar, 1, nyc, nxc)
-        for m in ("tiled", "per_cell", "per_cellvar"):
+        maps = ("tiled", "per_cell", "per_cellvar")
+        for m in maps:
             binding.flux_diff3d(*args, rhs=rhs, map=m)
-            t = timed(lambda: binding.flux_diff3d(*args, rhs=rhs, map=m), 10, True)
+        tg = timed_group({m: (lambda m=m: binding.flux_diff3d(*args, rhs=rhs, map=m)) for m in maps}, 10, True)
+        for m in maps:
             extra = None
             if cpu and m == "tiled":
                 extra = {"oracle": cpu_entry(lambda: oracle.flux_diff(fi.fx, fi.fy, None, fi.dx, fi.dy, None),
                                              cv, 3, "the whole workload")}
-            res[f"flux2d_4800x1200_x6_{m}"] = entry(t, cv, nbytes, extra)
+            res[f"flux2d_4800x1200_x6_{m}"] = entry(tg[m], cv, nbytes, extra)
             log("flux2d", m, res[f"flux2d_4800x1200_x6_{m}"])
         q0 = dev(inputs.normal_fields(nvar, nxc, nyc, 1, 1062))
         qs = dev(inputs.normal_fields(nvar, nxc, nyc, 1, 1063))
@@ -685,13 +718,14 @@ def measure_all(log, sections=frozenset({"all"}), cpu=True) -> dict:
         f = dev(fh)
         out = torch.empty(cv, dtype=torch.float64, device="cuda")
         for d, dn in ((0, "x"), (1, "y")):
-            for m in ("tiled", "per_cell", "per_cellvar"):
+            for m in maps:
                 binding.field_pack(f, d, out=out, map=m)
-                t = timed(lambda: binding.field_pack(f, d, out=out, map=m), 10, True)
+            tg = timed_group({m: (lambda m=m: binding.field_pack(f, d, out=out, map=m)) for m in maps}, 10, True)
+            for m in maps:
                 extra = None
                 if cpu and m == "tiled":
                     extra = {"oracle": cpu_entry(lambda: oracle.field_pack(fh, d), cv, 3, "the whole workload")}
-                res[f"pack2d_4800x1200_x6_{dn}_{m}"] = entry(t, cv, 16 * cv, extra)
+                res[f"pack2d_4800x1200_x6_{dn}_{m}"] = entry(tg[m], cv, 16 * cv, extra)
                 log("pack2d", dn, m, res[f"pack2d_4800x1200_x6_{dn}_{m}"])
         del f, out, fh
         torch.cuda.empty_cache()
