@@ -437,6 +437,7 @@ def measure_all(log, sections=frozenset({"all"}), cpu=True) -> dict:
         work, dtype) also the fraction of the vector-ALU peak."""
         med = statistics.median(times)
         d = {"ms": round(med * 1e3, 4), "ms_min": round(min(times) * 1e3, 4),
+             "ms_max": round(max(times) * 1e3, 4),
              "reps": len(times), "cellvar_per_s": float("%.4e" % (work / med)),
              "gbs_minimal": round(nbytes / med / 1e9, 1),
              "hbm_frac": round(nbytes / med / 1e9 / HBM_PEAK_GBS, 4)}
