@@ -7,8 +7,8 @@
 * Rows too long for even one tile row: the marching maps return SGC_ERANGE
   before anything is enqueued, so both buffers are untouched; the page's
   collapsed layout still runs the same grid.
-* The largest variable count (SGC_MAX_NVAR) through every pack direction and
-  the flux difference.
+* The largest variable count (SGC_MAX_NVAR) through every pack direction, the
+  flux difference and the fused SSPRK stage (2D and 3D).
 """
 import numpy as np
 import pytest
@@ -88,3 +88,27 @@ def test_max_nvar_flux():
         got = binding.flux_diff3d(dev(fi.fx), dev(fi.fy), dev(fi.fz), dev(fi.dx), dev(fi.dy),
                                   dev(fi.dz), map=m)
         assert_bitwise(host(got).reshape(-1), ref.reshape(-1), f"flux {m}")
+
+
+@pytest.mark.parametrize("two_d", [False, True])
+def test_max_nvar_flux_stage(two_d):
+    """The fused SSPRK stage carries six pointer tables (faces, q0, q, q')
+    in its kernel arguments; at the largest variable count, in 2D and 3D,
+    fresh and in place of q, every map gives the oracle's bits."""
+    nx, ny, nz = 31, 17, 1 if two_d else 13
+    fi = inputs.normal_faces(MAX_NVAR, nx, ny, nz, 1205, two_d=two_d)
+    q0 = inputs.normal_fields(MAX_NVAR, nx, ny, nz, 1206)
+    q = inputs.normal_fields(MAX_NVAR, nx, ny, nz, 1207)
+    say("max nvar stage", "2D" if two_d else "3D", fi.shape)
+    ref = oracle.flux_stage(fi.fx, fi.fy, fi.fz, fi.dx, fi.dy, fi.dz, q0, q, 0.75, 0.25, 1e-3)
+    rhs_ref = oracle.flux_diff(fi.fx, fi.fy, fi.fz, fi.dx, fi.dy, fi.dz)
+    for m in ("tiled", "per_cell", "per_cellvar"):
+        args = (dev(fi.fx), dev(fi.fy), dev(fi.fz) if fi.fz is not None else None, dev(fi.dx), dev(fi.dy),
+                dev(fi.dz) if fi.dz is not None else None)
+        rhs = binding.flux_diff3d(*args, map=m)
+        assert_bitwise(host(rhs).reshape(-1), rhs_ref.reshape(-1), f"flux {m}")
+        got = binding.flux_stage3d(*args, dev(q0), dev(q), 0.75, 0.25, 1e-3, map=m)
+        assert_bitwise(host(got).reshape(-1), ref.reshape(-1), f"stage {m}")
+        qd = dev(q)
+        binding.flux_stage3d(*args, dev(q0), qd, 0.75, 0.25, 1e-3, out=qd, map=m)
+        assert_bitwise(host(qd).reshape(-1), ref.reshape(-1), f"stage in place {m}")
